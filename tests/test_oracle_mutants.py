@@ -1,0 +1,75 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case plants one plausible slip in a private copy of oracle.c (a dropped
+term, a wrong sign, constant, rounding, index, bit order or code), builds it
+into a temporary library, and runs the pin suite against it in a child
+process.  The pin suite must fail for every mutant: a pin set that let one of
+them through would not be pinning the oracle.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+sys.path.insert(0, ROOT)
+from oracle.build import CFLAGS  # noqa: E402
+
+# (name, original text, replacement) -- each original must occur in oracle.c
+MUTANTS = [
+    ("gamma_drops_abs", "row += fabs((double)W[n * K + k]);", "row += ((double)W[n * K + k]);"),
+    ("gamma_wrong_n", "total / (double)(N * K)", "total / (double)(N * K + 1)"),
+    ("round_ties_away", "Wq[i] = (int8_t)nearbyint(t);", "Wq[i] = (int8_t)round(t);"),
+    ("no_clamp", "if (t > 1.0) t = 1.0;", ""),
+    ("code_minus_one", "if (q == -1) return 2;", "if (q == -1) return 3;"),
+    ("bit_order_msb_first", "<< (2 * j));", "<< (2 * (3 - j)));"),
+    ("decode_swapped", "if (code == 1) return 1;\n    if (code == 2) return -1;",
+     "if (code == 2) return 1;\n    if (code == 1) return -1;"),
+    ("bf16_shift", "(uint32_t)src[i] << 16;", "(uint32_t)src[i] << 15;"),
+    ("act_128", "float s = 127.0f / a;", "float s = 128.0f / a;"),
+    ("act_trunc", "float r = nearbyintf(p);", "float r = truncf(p);"),
+    ("act_scale_inverted", "d[m] = a / 127.0f;", "d[m] = 127.0f / a;"),
+    ("act_absmax_no_abs", "float ax = fabsf(x[k]);", "float ax = x[k];"),
+    ("acc_sub_as_add", "c -= Xq[m * K + k];", "c += Xq[m * K + k];"),
+    ("acc_wrong_index", "c += Xq[m * K + k];", "c += Xq[m * K + (k ^ 1)];"),
+    ("dequant_wrong_row_scale", "* (double)gamma * (double)d[m];", "* (double)gamma * (double)d[0];"),
+    ("ffn_drops_gate", "float h = Wu ? r2 * U[m * F + f] : r2;", "float h = r2;"),
+    ("ffn_relu_is_abs", "float r = G[m * F + f] > 0.0f ? G[m * F + f] : 0.0f;",
+     "float r = fabsf(G[m * F + f]);"),
+    ("ffn_rms_multiplies", "* (double)dh[m] / rms[m];", "* (double)dh[m] * rms[m];"),
+    ("ffn_rms_no_mean", "sqrt(ss / (double)F + (double)eps)", "sqrt(ss + (double)eps)"),
+    ("ffn_gain_dropped", "float z = norm_w ? h * norm_w[f] : h;", "float z = h;"),
+]
+
+
+def _run_mutant(name, old, new, src_text, tmpdir):
+    assert src_text.count(old) >= 1, f"{name}: pattern not found"
+    mut_c = os.path.join(tmpdir, f"{name}.c")
+    mut_so = os.path.join(tmpdir, f"{name}.so")
+    with open(mut_c, "w") as f:
+        f.write(src_text.replace(old, new, 1))
+    flags = [f for f in CFLAGS if f != "-Werror"]
+    subprocess.run(["gcc", *flags, mut_c, "-o", mut_so, "-lm"], check=True,
+                   capture_output=True)
+    env = dict(os.environ, BITLINEAR_ORACLE_LIB=mut_so, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(HERE, "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode, r.stdout[-400:]
+
+
+def test_every_mutant_is_caught():
+    with open(SRC) as f:
+        src_text = f.read()
+    with tempfile.TemporaryDirectory() as tmpdir:
+        with cf.ThreadPoolExecutor(max_workers=4) as ex:
+            results = list(ex.map(lambda m: _run_mutant(*m, src_text, tmpdir), MUTANTS))
+    survivors = [(n, out) for n, rc, out in results if rc == 0]
+    assert not survivors, f"mutants not caught by the pins: {survivors}"
+    broken = [(n, rc) for n, rc, _ in results if rc not in (1,)]
+    assert not broken, f"mutant runs ended abnormally (not a test failure): {broken}"
