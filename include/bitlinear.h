@@ -1,0 +1,213 @@
+/*
+ * bitlinear.h -- C ABI of libbitlinear, the BitLinear W1.58A8 layer of
+ * BitNet b1.58 on AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (nn.Linear convention, no bias):
+ *     X [M][K] activations, W [N][K] weights, Y [M][N] = X W^T.
+ * W is quantised by absmean to ternary codes with one scale gamma per tensor,
+ * X is quantised per token (row) by absmax to int8 with one scale d[m], the
+ * product is an exact int32 sum and Y = acc * gamma * d[m].
+ *
+ * Passages defining the operations (pages by title, section):
+ *   [RPT]  "Microsoft BitNet 深度研究报告", §2 技术原理:
+ *          (1) 三元量化 -- weights take the values {-1, 0, +1};
+ *          (2) AbsMean 量化 -- Q(w) = round(clamp(w / gamma, -1, 1)),
+ *              gamma = (1/n) sum |w_i|; 实际存储 -- 2-bit codes
+ *              {0: 0, +1: 1, -1: 2};
+ *          (3) 查找表优化 -- W = +1: C += A, W = -1: C -= A, W = 0: skip.
+ *   [CARD] "BitNet b1.58 2B4T - 原生1比特大语言模型规模化实践", 模型详情 --
+ *          W1.58A8; absmean ternary weights; per-token absmax int8
+ *          activations; ReLU² FFN; subln; no bias in linear or norm layers.
+ *   [NEWS] iaiol.com BitNet b1.58 2B4T article, "权重映射为三元值{-1, 0, +1}"
+ *          -- per-token absmax 8-bit activations, subln, ReLU² instead of
+ *          SwiGLU; "微软在1 bit LLM上的探索" -- BitLinear replaces nn.Linear,
+ *          W1.58A8 needs its own matmul kernel.
+ *   [TR]   copy of the "BitNet b1.58 2B4T Technical Report", 推理完满 /
+ *          GPU端 -- four ternary weights packed into one int8; pack, store,
+ *          load, unpack, compute.
+ *
+ * Data formats (readings of what the pages leave open):
+ *   packed weights Wp: uint8 [N][K/4], row-major.  Byte b of row n holds the
+ *     weights k = 4b..4b+3; weight 4b+j sits in bits 2j..2j+1; code 0 = 0,
+ *     1 = +1, 2 = -1 (code 3 is never written and reads as 0).
+ *   gamma: one fp32 per weight tensor, = fp32(fp64 sum |W| / (N*K)), the sum
+ *     taken row by row in ascending k and then over rows in ascending n.
+ *     Wq = sign(w) where 2|w| > gamma, else 0 (round half to even).
+ *   Xq: int8 [M][K] row-major, d: fp32 [M].  Per row: a = max|x|,
+ *     s = fp32(127 / a), Xq = clamp(rne(fp32(x * s)), -127, 127),
+ *     d = fp32(a / 127); an all-zero row gives Xq = 0, d = 0.
+ *   acc: int32 [M][N], exact (|acc| <= 127 K < 2^31).
+ *   Y: fp32 [M][N], Y = fp32(float(acc) * fp32(gamma * d[m])).
+ *
+ * Calling conventions, for every call below:
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA
+ *     memory) on the current HIP device; the caller owns all memory and the
+ *     stream.  The library keeps no pointer after it returns and never
+ *     allocates or frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; no call synchronises the host.
+ *   - Validation runs on the host before anything is enqueued.  On a non-OK
+ *     return nothing was launched and no output was written;
+ *     bl_last_error() then gives a readable reason (per thread).
+ *   - Tensor pointers must be 16-byte aligned (BL_ERR_ALIGN), except d,
+ *     gamma and the fp32 vectors, which need 4-byte alignment.
+ *   - Device faults inside a kernel surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - Inputs with NaN or Inf give unspecified (but memory-safe) results.
+ *   - The current device must be gfx950 (BL_ERR_ARCH).
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BL_ABI_VERSION 1
+
+typedef enum {
+    BL_OK = 0,
+    BL_ERR_NULL = 1,      /* a required pointer is NULL */
+    BL_ERR_SHAPE = 2,     /* a size is negative, too large, or not a required multiple */
+    BL_ERR_DTYPE = 3,     /* unknown bl_dtype */
+    BL_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
+    BL_ERR_WORKSPACE = 5, /* ws is NULL or ws_bytes < bl_workspace_bytes(...) */
+    BL_ERR_ARCH = 6,      /* the current HIP device is not gfx950 */
+    BL_ERR_HIP = 7        /* a HIP runtime call or a kernel launch failed */
+} bl_status;
+
+typedef enum {
+    BL_F32 = 0,           /* IEEE binary32 */
+    BL_BF16 = 1           /* bfloat16 (upper half of binary32) */
+} bl_dtype;
+
+typedef enum {
+    BL_OP_QUANT_WEIGHT = 0,   /* quant_weight_absmean_pack */
+    BL_OP_FFN_RELU2 = 1       /* bitlinear_ffn_relu2 */
+} bl_op;
+
+/* Largest K (and F) any call accepts: keeps |acc| <= 127 K exact in int32
+ * and float(acc) exact in fp32 (127 K <= 2^24). */
+#define BL_MAX_K 131072
+
+/* ------------------------------------------------------------------------
+ * quant_weight_absmean_pack -- offline weight path.
+ * [RPT] §2 (2) AbsMean 量化 (gamma, Q(w)) and 实际存储 (codes);
+ * [TR] GPU端 (four weights per int8).
+ *
+ *   W      in   fp32 [N][K], row-major (the nn.Linear weight, out x in).
+ *   N, K        N >= 0, K >= 0, K % 4 == 0, K <= BL_MAX_K.
+ *   Wp     out  uint8 [N][K/4], the packed codes (format above).
+ *   gamma  out  fp32 [1]; N*K == 0 gives gamma = 0 and writes no Wp byte.
+ *   ws          device workspace of >= bl_workspace_bytes(BL_OP_QUANT_WEIGHT,
+ *               0, N, K, 0) bytes (N fp64 row sums), 16-byte aligned.
+ * gamma is reproducible to the bit (fixed summation order).
+ */
+bl_status quant_weight_absmean_pack(const float *W, int64_t N, int64_t K,
+                                    uint8_t *Wp, float *gamma,
+                                    void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * quant_act_absmax_i8 -- per-token absmax int8 activation quantisation.
+ * [NEWS] 权重映射为三元值; [CARD] 模型详情 (per-token absmax, 8-bit).
+ *
+ *   X      in   [M][K] row-major, element type `dtype` (BL_F32 or BL_BF16).
+ *   M, K        M >= 0, K >= 0, K <= BL_MAX_K.
+ *   Xq     out  int8 [M][K].
+ *   d      out  fp32 [M], the per-token scale a / 127 (0 for a zero row).
+ * Bit-exact with the formula in the header comment.
+ */
+bl_status quant_act_absmax_i8(const void *X, bl_dtype dtype, int64_t M, int64_t K,
+                              int8_t *Xq, float *d, void *stream);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_gemv -- decode-sized W1.58A8 product, M = 1..64 tokens.
+ * [RPT] §2 (3) 查找表优化 (add / subtract / skip); [TR] GPU端 (load the
+ * packed weights, unpack, compute); [CARD] 模型详情 (W1.58A8).
+ *
+ *   Xq     in   int8 [M][K];  d  in  fp32 [M]  (from quant_act_absmax_i8).
+ *   M           1 <= M <= 64 (M == 0 is a no-op returning BL_OK).
+ *   Wp     in   uint8 [N][K/4];  gamma  in  fp32 [1]  (device).
+ *   N, K        N >= 0; K % 64 == 0; K <= BL_MAX_K.
+ *   Y      out  fp32 [M][N] = float(acc) * fp32(gamma * d[m]).
+ *   acc    out  int32 [M][N], optional (NULL = not written): the exact
+ *               accumulator sum_k Xq[m][k] * Wq[n][k].
+ * Streams the packed weights once per launch; acc and Y are bit-exact.
+ */
+bl_status bitlinear_gemv(const int8_t *Xq, const float *d, int64_t M,
+                         const uint8_t *Wp, const float *gamma, int64_t N, int64_t K,
+                         float *Y, int32_t *acc, void *stream);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_gemm -- prefill-sized W1.58A8 product, any M >= 0, on int8
+ * matrix cores: the packed tiles are unpacked to int8 and multiplied with
+ * int32 accumulation, with the rescale fused into the epilogue.
+ * Same arguments, formats and results as bitlinear_gemv, except that M has
+ * no upper bound (M <= 2^31 - 1).
+ */
+bl_status bitlinear_gemm(const int8_t *Xq, const float *d, int64_t M,
+                         const uint8_t *Wp, const float *gamma, int64_t N, int64_t K,
+                         float *Y, int32_t *acc, void *stream);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_ffn_relu2 -- the feed-forward tail of a BitNet b1.58 block:
+ * ReLU² (gated) + subln RMSNorm + int8 requantisation + down projection.
+ * [NEWS] 权重映射为三元值 (ReLU² in place of SwiGLU; subln);
+ * [CARD] 模型详情 (ReLU², subln, no biases, W1.58A8 in every BitLinear).
+ *
+ * Readings (the pages print no formula for ReLU² gating or subln):
+ *   G = Xq Wg^T and U = Xq Wu^T as W1.58A8 BitLinears (fp32, as Y above);
+ *   H = fp32(fp32(r * r) * U) with r = max(G, 0)   (Wu == NULL: H = r * r);
+ *   subln: Z = H / rms * g, rms = sqrt(sum_f H^2 / F + eps), g = norm_w
+ *          (NULL = ones);
+ *   Z is requantised per token (absmax int8) and Y = Zq Wd^T (W1.58A8).
+ * Absmax codes do not change when a row is scaled by 1/rms > 0, so the int8
+ * codes Hq are taken from fp32(H * g) and Z's scale is dh / rms, where dh is
+ * the absmax scale of H * g.  Hq and dh are bit-exact; Y carries the rms sum,
+ * whose summation order is the library's (fp32 relative error ~1e-6).
+ *
+ *   Xq, d       in   int8 [M][K], fp32 [M] (the block input, quantised).
+ *   M, K, F, N       M >= 0; K % 64 == 0; F % 64 == 0; N >= 0; K, F <= BL_MAX_K.
+ *   Wg, gamma_g in   uint8 [F][K/4], fp32 [1].
+ *   Wu, gamma_u in   uint8 [F][K/4], fp32 [1]; Wu == NULL: ungated
+ *                    (gamma_u ignored).
+ *   norm_w      in   fp32 [F] or NULL.
+ *   eps              RMSNorm epsilon (>= 0), e.g. 1e-5.
+ *   Wd, gamma_d in   uint8 [N][F/4], fp32 [1].
+ *   Y           out  fp32 [M][N].
+ *   Hq          out  int8 [M][F], optional (NULL = not written).
+ *   dh          out  fp32 [M], optional (NULL = not written).
+ *   ws               >= bl_workspace_bytes(BL_OP_FFN_RELU2, M, N, K, F)
+ *                    bytes of device memory, 16-byte aligned.
+ */
+bl_status bitlinear_ffn_relu2(const int8_t *Xq, const float *d,
+                              int64_t M, int64_t K, int64_t F,
+                              const uint8_t *Wg, const float *gamma_g,
+                              const uint8_t *Wu, const float *gamma_u,
+                              const float *norm_w, float eps,
+                              const uint8_t *Wd, const float *gamma_d, int64_t N,
+                              float *Y, int8_t *Hq, float *dh,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes a call needs for the given sizes (0 for calls that need
+ * none; arguments a call does not use are ignored). */
+size_t bl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t F);
+
+/* Static, never NULL. */
+const char *bl_status_string(bl_status status);
+
+/* Detail of this thread's last non-OK return ("" if none).  Valid until the
+ * thread's next call into the library. */
+const char *bl_last_error(void);
+
+/* BL_ABI_VERSION of the built library. */
+int bl_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

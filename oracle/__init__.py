@@ -32,6 +32,8 @@ def _load():
             _build.build()
         path = _build.LIB
     lib = ctypes.CDLL(path)
+    lib.ob_num_threads.restype = ctypes.c_int
+    lib.ob_num_threads.argtypes = []
     lib.ob_absmean_gamma.restype = _f32
     lib.ob_absmean_gamma.argtypes = [_p, _i64, _i64]
     lib.ob_ternarize.restype = None
@@ -66,6 +68,11 @@ def _c(a, dtype):
 
 def _ptr(a):
     return a.ctypes.data_as(_p) if a is not None else None
+
+
+def num_threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().ob_num_threads())
 
 
 def absmean_gamma(W):

@@ -35,11 +35,15 @@
  * Parity pins for every function live in tests/test_oracle_pins.py.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <string.h>
 
 #define OB_EXPORT __attribute__((visibility("default")))
+
+/* Threads the OpenMP loops below use (reported with CPU timings). */
+OB_EXPORT int ob_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------------- */
 /* [RPT] §2 (2) AbsMean 量化:  gamma = (1/n) * sum_i |w_i|.
@@ -258,7 +262,7 @@ OB_EXPORT void ob_dequant_f32(const int32_t *acc, const float *d, float gamma,
  *     Z'     = fl32(H * g)                      (Z' = H when g is NULL)
  *     Hq, dh = ob_quant_act(Z')
  *     rms    = sqrt(sum_f H^2 / F + eps)        (fp64)
- *     Y      = acc_d * gamma_d * dh / rms       (fp64)
+ *     Y      = acc_d * gamma_d * (dh / rms)     (fp64; 0 where dh == 0)
  * Outputs: Y [M][N] fp64, Hq [M][F] int8, dh [M] fp32, rms [M] fp64. */
 OB_EXPORT void ob_ffn_relu2(const int8_t *Xq, const float *d, int64_t M, int64_t K, int64_t F,
                             const uint8_t *Wg, float gamma_g,
@@ -290,8 +294,10 @@ OB_EXPORT void ob_ffn_relu2(const int8_t *Xq, const float *d, int64_t M, int64_t
     }
     ob_quant_act(Zp, M, F, Hq, dh);
     ob_ternary_acc(Hq, Wd, M, N, F, acc_scratch);
-    for (int64_t m = 0; m < M; ++m)
+    for (int64_t m = 0; m < M; ++m) {
+        /* Z's scale; a row whose H * g is all zero has Zq = 0 and scale 0. */
+        double dz = dh[m] > 0.0f ? (double)dh[m] / rms[m] : 0.0;
         for (int64_t n = 0; n < N; ++n)
-            Y[m * N + n] = (double)acc_scratch[m * N + n] * (double)gamma_d
-                           * (double)dh[m] / rms[m];
+            Y[m * N + n] = (double)acc_scratch[m * N + n] * (double)gamma_d * dz;
+    }
 }

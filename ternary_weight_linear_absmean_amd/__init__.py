@@ -1,0 +1,11 @@
+"""libbitlinear: BitLinear W1.58A8 (BitNet b1.58) on AMD Instinct MI355X.
+
+Python names match the C entry points of include/bitlinear.h; see _native.py.
+Importing the package does not load the native library; the first call (or
+``load()``) does, and raises if it has not been built.
+"""
+from ._native import (  # noqa: F401
+    BL_BF16, BL_F32, BL_MAX_K, BL_OP_FFN_RELU2, BL_OP_QUANT_WEIGHT, EXPORTS, LIB_PATH,
+    BitLinearError, bitlinear_ffn_relu2, bitlinear_gemm, bitlinear_gemv, load,
+    quant_act_absmax_i8, quant_weight_absmean_pack, workspace_bytes,
+)

@@ -1,0 +1,208 @@
+"""ctypes binding of libbitlinear (include/bitlinear.h).
+
+Argument marshalling only: each function checks that its torch tensors are on
+the GPU, contiguous and of the right dtype, allocates outputs (and the
+workspace) with torch when the caller gives none, and passes raw device
+pointers and the current HIP stream to the C entry point of the same name.
+Every step of the computation runs in libbitlinear's kernels.  There is no
+fallback: if the library is missing, ``load()`` raises.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbitlinear.so")
+
+BL_F32 = 0
+BL_BF16 = 1
+BL_OP_QUANT_WEIGHT = 0
+BL_OP_FFN_RELU2 = 1
+BL_MAX_K = 131072
+
+STATUS = {0: "BL_OK", 1: "BL_ERR_NULL", 2: "BL_ERR_SHAPE", 3: "BL_ERR_DTYPE",
+          4: "BL_ERR_ALIGN", 5: "BL_ERR_WORKSPACE", 6: "BL_ERR_ARCH", 7: "BL_ERR_HIP"}
+
+EXPORTS = ["quant_weight_absmean_pack", "quant_act_absmax_i8", "bitlinear_gemv",
+           "bitlinear_gemm", "bitlinear_ffn_relu2", "bl_workspace_bytes",
+           "bl_status_string", "bl_last_error", "bl_abi_version"]
+
+_lib = None
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, call, status, detail):
+        self.call, self.status, self.detail = call, status, detail
+        super().__init__(f"{call}: {STATUS.get(status, status)}: {detail}")
+
+
+def load():
+    """Load libbitlinear.so (built in-tree by build.py); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python -m ternary_weight_linear_absmean_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    st = ctypes.c_int
+    lib.quant_weight_absmean_pack.restype = st
+    lib.quant_weight_absmean_pack.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
+    lib.quant_act_absmax_i8.restype = st
+    lib.quant_act_absmax_i8.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p]
+    for name in ("bitlinear_gemv", "bitlinear_gemm"):
+        f = getattr(lib, name)
+        f.restype = st
+        f.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _p]
+    lib.bitlinear_ffn_relu2.restype = st
+    lib.bitlinear_ffn_relu2.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p,
+                                        ctypes.c_float, _p, _p, _i64, _p, _p, _p, _p, _sz, _p]
+    lib.bl_workspace_bytes.restype = _sz
+    lib.bl_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64]
+    lib.bl_status_string.restype = ctypes.c_char_p
+    lib.bl_status_string.argtypes = [ctypes.c_int]
+    lib.bl_last_error.restype = ctypes.c_char_p
+    lib.bl_last_error.argtypes = []
+    lib.bl_abi_version.restype = ctypes.c_int
+    lib.bl_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(call, status):
+    if status != 0:
+        raise BitLinearError(call, status, load().bl_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def workspace_bytes(op, M=0, N=0, K=0, F=0):
+    return int(load().bl_workspace_bytes(op, M, N, K, F))
+
+
+def quant_weight_absmean_pack(W, Wp=None, gamma=None, ws=None, stream=None):
+    """fp32 W [N, K] -> (packed uint8 [N, K/4], gamma fp32 [1]) on the GPU."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    dev = W.device
+    Wp = _dev(Wp, torch.uint8, "Wp") if Wp is not None else torch.empty(
+        (N, K // 4), dtype=torch.uint8, device=dev)
+    gamma = _dev(gamma, torch.float32, "gamma") if gamma is not None else torch.empty(
+        (1,), dtype=torch.float32, device=dev)
+    need = workspace_bytes(BL_OP_QUANT_WEIGHT, 0, N, K, 0)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check("quant_weight_absmean_pack", load().quant_weight_absmean_pack(
+        _ptr(W), N, K, _ptr(Wp), _ptr(gamma), _ptr(ws), ws.numel(), _stream(stream)))
+    return Wp, gamma
+
+
+def quant_act_absmax_i8(X, Xq=None, d=None, stream=None):
+    """X [M, K] (fp32 or bf16) -> (Xq int8 [M, K], d fp32 [M])."""
+    if X.dtype == torch.float32:
+        dt = BL_F32
+    elif X.dtype == torch.bfloat16:
+        dt = BL_BF16
+    else:
+        raise TypeError("X must be float32 or bfloat16")
+    _dev(X, X.dtype, "X")
+    M, K = X.shape
+    Xq = _dev(Xq, torch.int8, "Xq") if Xq is not None else torch.empty(
+        (M, K), dtype=torch.int8, device=X.device)
+    d = _dev(d, torch.float32, "d") if d is not None else torch.empty(
+        (M,), dtype=torch.float32, device=X.device)
+    _check("quant_act_absmax_i8", load().quant_act_absmax_i8(
+        _ptr(X), dt, M, K, _ptr(Xq), _ptr(d), _stream(stream)))
+    return Xq, d
+
+
+def _product(call, Xq, d, Wp, gamma, Y, acc, want_acc, stream):
+    _dev(Xq, torch.int8, "Xq")
+    _dev(d, torch.float32, "d")
+    _dev(Wp, torch.uint8, "Wp")
+    _dev(gamma, torch.float32, "gamma")
+    M, K = Xq.shape
+    N = Wp.shape[0]
+    if Wp.dim() != 2 or Wp.shape[1] * 4 != K:
+        raise ValueError(f"Wp must be [N, K/4] = [*, {K // 4}], got {tuple(Wp.shape)}")
+    if d.shape != (M,):
+        raise ValueError("d must be [M]")
+    Y = _dev(Y, torch.float32, "Y") if Y is not None else torch.empty(
+        (M, N), dtype=torch.float32, device=Xq.device)
+    if acc is None and want_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    _dev(acc, torch.int32, "acc")
+    _check(call, getattr(load(), call)(_ptr(Xq), _ptr(d), M, _ptr(Wp), _ptr(gamma), N, K,
+                                       _ptr(Y), _ptr(acc), _stream(stream)))
+    return (Y, acc) if want_acc or acc is not None else Y
+
+
+def bitlinear_gemv(Xq, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=None):
+    """Y [M, N] fp32 for 1 <= M <= 64 tokens; with want_acc also int32 acc."""
+    return _product("bitlinear_gemv", Xq, d, Wp, gamma, Y, acc, want_acc, stream)
+
+
+def bitlinear_gemm(Xq, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=None):
+    """Y [M, N] fp32 for any M on int8 MFMA; with want_acc also int32 acc."""
+    return _product("bitlinear_gemm", Xq, d, Wp, gamma, Y, acc, want_acc, stream)
+
+
+def bitlinear_ffn_relu2(Xq, d, Wg, gamma_g, Wu, gamma_u, Wd, gamma_d, norm_w=None, eps=1e-5,
+                        Y=None, Hq=None, dh=None, want_debug=False, ws=None, stream=None):
+    """ReLU^2 FFN tail; returns Y [M, N] (and Hq int8 [M, F], dh fp32 [M] with
+    want_debug)."""
+    _dev(Xq, torch.int8, "Xq")
+    _dev(d, torch.float32, "d")
+    for t, n in ((Wg, "Wg"), (Wd, "Wd")):
+        _dev(t, torch.uint8, n)
+    _dev(Wu, torch.uint8, "Wu")
+    _dev(gamma_g, torch.float32, "gamma_g")
+    _dev(gamma_d, torch.float32, "gamma_d")
+    _dev(gamma_u, torch.float32, "gamma_u")
+    _dev(norm_w, torch.float32, "norm_w")
+    M, K = Xq.shape
+    F = Wg.shape[0]
+    N = Wd.shape[0]
+    if Wg.shape[1] * 4 != K or (Wu is not None and tuple(Wu.shape) != tuple(Wg.shape)) \
+            or Wd.shape[1] * 4 != F:
+        raise ValueError("weight shapes do not chain: Wg/Wu [F, K/4], Wd [N, F/4]")
+    dev = Xq.device
+    Y = _dev(Y, torch.float32, "Y") if Y is not None else torch.empty(
+        (M, N), dtype=torch.float32, device=dev)
+    if want_debug:
+        Hq = Hq if Hq is not None else torch.empty((M, F), dtype=torch.int8, device=dev)
+        dh = dh if dh is not None else torch.empty((M,), dtype=torch.float32, device=dev)
+    _dev(Hq, torch.int8, "Hq")
+    _dev(dh, torch.float32, "dh")
+    need = workspace_bytes(BL_OP_FFN_RELU2, M, N, K, F)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check("bitlinear_ffn_relu2", load().bitlinear_ffn_relu2(
+        _ptr(Xq), _ptr(d), M, K, F, _ptr(Wg), _ptr(gamma_g), _ptr(Wu), _ptr(gamma_u),
+        _ptr(norm_w), float(eps), _ptr(Wd), _ptr(gamma_d), N, _ptr(Y), _ptr(Hq), _ptr(dh),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return (Y, Hq, dh) if want_debug else Y

@@ -1,0 +1,290 @@
+// api.cpp -- the C ABI of libbitlinear (declared in include/bitlinear.h).
+//
+// Every entry point validates its arguments on the host, in a fixed order
+// (sizes, then the no-op case, then pointers, alignment, workspace, device
+// architecture), and only then enqueues kernels on the caller's stream.  No
+// entry point allocates, frees or synchronises.  The only global state is a
+// per-device cache of "is this device gfx950", filled on first use.
+#include "bitlinear.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "launch.h"
+
+#define BL_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512];
+
+bl_status fail(bl_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bl_status ok() {
+    g_last_error[0] = '\0';
+    return BL_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_arch_mutex;
+signed char g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+bl_status check_arch() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(BL_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BL_ERR_ARCH, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_arch_mutex);
+    if (g_arch_state[dev] == 0) {
+        hipDeviceProp_t p;
+        e = hipGetDeviceProperties(&p, dev);
+        if (e != hipSuccess)
+            return fail(BL_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+        g_arch_state[dev] = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+        if (g_arch_state[dev] < 0)
+            return fail(BL_ERR_ARCH, "device %d is %s, not gfx950", dev, p.gcnArchName);
+    }
+    if (g_arch_state[dev] < 0)
+        return fail(BL_ERR_ARCH, "device %d is not gfx950", dev);
+    return BL_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bl_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(BL_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// FFN workspace: G [M][F] f32 | U [M][F] f32 | Hq [M][F] i8 | dh [M] f32 | dz [M] f32.
+struct FfnWs {
+    size_t g, u, hq, dh, dz, total;
+};
+
+FfnWs ffn_ws(int64_t M, int64_t F) {
+    FfnWs w;
+    const size_t mf = (size_t)M * (size_t)F;
+    w.g = 0;
+    w.u = round_up(w.g + mf * 4, 256);
+    w.hq = round_up(w.u + mf * 4, 256);
+    w.dh = round_up(w.hq + mf, 256);
+    w.dz = round_up(w.dh + (size_t)M * 4, 256);
+    w.total = round_up(w.dz + (size_t)M * 4, 256);
+    return w;
+}
+
+// Shared checks of the BitLinear product calls.
+bl_status check_product(const char *name, const int8_t *Xq, const float *d, int64_t M,
+                        int64_t max_m, const uint8_t *Wp, const float *gamma, int64_t N,
+                        int64_t K, float *Y, int32_t *acc, bool *noop) {
+    *noop = false;
+    if (M < 0 || N < 0 || K < 0)
+        return fail(BL_ERR_SHAPE, "%s: negative size (M=%lld N=%lld K=%lld)", name,
+                    (long long)M, (long long)N, (long long)K);
+    if (M > max_m)
+        return fail(BL_ERR_SHAPE, "%s: M=%lld exceeds %lld", name, (long long)M,
+                    (long long)max_m);
+    if (N > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: N=%lld exceeds 2^31-1", name, (long long)N);
+    if (K > BL_MAX_K || K % 64 != 0)
+        return fail(BL_ERR_SHAPE, "%s: K=%lld must be a multiple of 64 and <= %d", name,
+                    (long long)K, BL_MAX_K);
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return ok();
+    }
+    if (!Xq || !d || !Wp || !gamma || !Y)
+        return fail(BL_ERR_NULL, "%s: NULL pointer (Xq=%p d=%p Wp=%p gamma=%p Y=%p)", name,
+                    (const void *)Xq, (const void *)d, (const void *)Wp, (const void *)gamma,
+                    (const void *)Y);
+    if (!aligned(Xq, 16) || !aligned(Wp, 16))
+        return fail(BL_ERR_ALIGN, "%s: Xq and Wp must be 16-byte aligned", name);
+    if (!aligned(d, 4) || !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+        return fail(BL_ERR_ALIGN, "%s: d, gamma, Y and acc must be 4-byte aligned", name);
+    return check_arch();
+}
+
+}  // namespace
+
+BL_EXPORT const char *bl_status_string(bl_status st) {
+    switch (st) {
+    case BL_OK: return "BL_OK";
+    case BL_ERR_NULL: return "BL_ERR_NULL";
+    case BL_ERR_SHAPE: return "BL_ERR_SHAPE";
+    case BL_ERR_DTYPE: return "BL_ERR_DTYPE";
+    case BL_ERR_ALIGN: return "BL_ERR_ALIGN";
+    case BL_ERR_WORKSPACE: return "BL_ERR_WORKSPACE";
+    case BL_ERR_ARCH: return "BL_ERR_ARCH";
+    case BL_ERR_HIP: return "BL_ERR_HIP";
+    }
+    return "BL_ERR_UNKNOWN";
+}
+
+BL_EXPORT const char *bl_last_error(void) { return g_last_error; }
+
+BL_EXPORT int bl_abi_version(void) { return BL_ABI_VERSION; }
+
+BL_EXPORT size_t bl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t F) {
+    (void)K;
+    if (M < 0 || N < 0 || F < 0)
+        return 0;
+    switch (op) {
+    case BL_OP_QUANT_WEIGHT: return round_up((size_t)N * sizeof(double), 256);
+    case BL_OP_FFN_RELU2: return ffn_ws(M, F).total;
+    default: return 0;
+    }
+}
+
+BL_EXPORT bl_status quant_weight_absmean_pack(const float *W, int64_t N, int64_t K, uint8_t *Wp,
+                                              float *gamma, void *ws, size_t ws_bytes,
+                                              void *stream) {
+    const char *name = "quant_weight_absmean_pack";
+    if (N < 0 || K < 0 || K % 4 != 0 || K > BL_MAX_K || N > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: need N in [0, 2^31), K in [0, %d] with K %% 4 == 0 "
+                    "(N=%lld K=%lld)", name, BL_MAX_K, (long long)N, (long long)K);
+    if (!gamma)
+        return fail(BL_ERR_NULL, "%s: gamma is NULL", name);
+    if (!aligned(gamma, 4))
+        return fail(BL_ERR_ALIGN, "%s: gamma must be 4-byte aligned", name);
+    const bool empty = (N == 0 || K == 0);
+    if (!empty) {
+        if (!W || !Wp)
+            return fail(BL_ERR_NULL, "%s: NULL pointer (W=%p Wp=%p)", name, (const void *)W,
+                        (const void *)Wp);
+        if (!aligned(W, 16) || !aligned(Wp, 16))
+            return fail(BL_ERR_ALIGN, "%s: W and Wp must be 16-byte aligned", name);
+        const size_t need = bl_workspace_bytes(BL_OP_QUANT_WEIGHT, 0, N, K, 0);
+        if (!ws || ws_bytes < need)
+            return fail(BL_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", name,
+                        ws_bytes, ws, need);
+        if (!aligned(ws, 16))
+            return fail(BL_ERR_ALIGN, "%s: ws must be 16-byte aligned", name);
+    }
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+    return launched(bl::launch_quant_weight(W, N, K, Wp, gamma, static_cast<double *>(ws),
+                                            static_cast<hipStream_t>(stream)),
+                    name);
+}
+
+BL_EXPORT bl_status quant_act_absmax_i8(const void *X, bl_dtype dtype, int64_t M, int64_t K,
+                                        int8_t *Xq, float *d, void *stream) {
+    const char *name = "quant_act_absmax_i8";
+    if (M < 0 || K < 0 || K > BL_MAX_K || M > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: need M in [0, 2^31), K in [0, %d] (M=%lld K=%lld)", name,
+                    BL_MAX_K, (long long)M, (long long)K);
+    if (dtype != BL_F32 && dtype != BL_BF16)
+        return fail(BL_ERR_DTYPE, "%s: unknown dtype %d", name, (int)dtype);
+    if (M == 0)
+        return ok();
+    if (!d || (K > 0 && (!X || !Xq)))
+        return fail(BL_ERR_NULL, "%s: NULL pointer (X=%p Xq=%p d=%p)", name, X, (void *)Xq,
+                    (void *)d);
+    if ((K > 0 && (!aligned(X, 16) || !aligned(Xq, 16))) || !aligned(d, 4))
+        return fail(BL_ERR_ALIGN, "%s: X and Xq must be 16-byte aligned, d 4-byte", name);
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+    return launched(bl::launch_quant_act(X, dtype == BL_BF16 ? 1 : 0, M, K, Xq, d,
+                                         static_cast<hipStream_t>(stream)),
+                    name);
+}
+
+BL_EXPORT bl_status bitlinear_gemv(const int8_t *Xq, const float *d, int64_t M, const uint8_t *Wp,
+                                   const float *gamma, int64_t N, int64_t K, float *Y,
+                                   int32_t *acc, void *stream) {
+    bool noop = false;
+    bl_status st = check_product("bitlinear_gemv", Xq, d, M, 64, Wp, gamma, N, K, Y, acc, &noop);
+    if (st != BL_OK || noop)
+        return st;
+    return launched(bl::launch_bitlinear(Xq, d, (int)M, Wp, gamma, (int)N, (int)K, Y, acc,
+                                         static_cast<hipStream_t>(stream)),
+                    "bitlinear_gemv");
+}
+
+BL_EXPORT bl_status bitlinear_gemm(const int8_t *Xq, const float *d, int64_t M, const uint8_t *Wp,
+                                   const float *gamma, int64_t N, int64_t K, float *Y,
+                                   int32_t *acc, void *stream) {
+    bool noop = false;
+    bl_status st =
+        check_product("bitlinear_gemm", Xq, d, M, kI32Max, Wp, gamma, N, K, Y, acc, &noop);
+    if (st != BL_OK || noop)
+        return st;
+    return launched(bl::launch_gemm(Xq, d, (int)M, Wp, gamma, (int)N, (int)K, Y, acc,
+                                    static_cast<hipStream_t>(stream)),
+                    "bitlinear_gemm");
+}
+
+BL_EXPORT bl_status bitlinear_ffn_relu2(const int8_t *Xq, const float *d, int64_t M, int64_t K,
+                                        int64_t F, const uint8_t *Wg, const float *gamma_g,
+                                        const uint8_t *Wu, const float *gamma_u,
+                                        const float *norm_w, float eps, const uint8_t *Wd,
+                                        const float *gamma_d, int64_t N, float *Y, int8_t *Hq,
+                                        float *dh, void *ws, size_t ws_bytes, void *stream) {
+    const char *name = "bitlinear_ffn_relu2";
+    if (M < 0 || N < 0 || K < 0 || F < 0 || M > kI32Max || N > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: negative or too large size (M=%lld K=%lld F=%lld N=%lld)",
+                    name, (long long)M, (long long)K, (long long)F, (long long)N);
+    if (K % 64 != 0 || F % 64 != 0 || K > BL_MAX_K || F > BL_MAX_K)
+        return fail(BL_ERR_SHAPE, "%s: K=%lld and F=%lld must be multiples of 64 and <= %d", name,
+                    (long long)K, (long long)F, BL_MAX_K);
+    if (!(eps >= 0.0f))
+        return fail(BL_ERR_SHAPE, "%s: eps must be >= 0", name);
+    if (M == 0)
+        return ok();
+    if (!Xq || !d || !Wg || !gamma_g || !Wd || !gamma_d || (N > 0 && !Y) || (Wu && !gamma_u))
+        return fail(BL_ERR_NULL, "%s: NULL pointer", name);
+    if (!aligned(Xq, 16) || !aligned(Wg, 16) || !aligned(Wd, 16) || (Wu && !aligned(Wu, 16)) ||
+        (Hq && !aligned(Hq, 16)))
+        return fail(BL_ERR_ALIGN, "%s: Xq, Wg, Wu, Wd and Hq must be 16-byte aligned", name);
+    if (!aligned(d, 4) || !aligned(gamma_g, 4) || !aligned(gamma_d, 4) ||
+        (gamma_u && !aligned(gamma_u, 4)) || (norm_w && !aligned(norm_w, 16)) ||
+        (Y && !aligned(Y, 4)) || (dh && !aligned(dh, 4)))
+        return fail(BL_ERR_ALIGN, "%s: fp32 vectors must be 4-byte aligned (norm_w 16)", name);
+    const FfnWs w = ffn_ws(M, F);
+    if (!ws || ws_bytes < w.total)
+        return fail(BL_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", name, ws_bytes,
+                    ws, w.total);
+    if (!aligned(ws, 16))
+        return fail(BL_ERR_ALIGN, "%s: ws must be 16-byte aligned", name);
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+    float *G = reinterpret_cast<float *>(base + w.g);
+    float *U = Wu ? reinterpret_cast<float *>(base + w.u) : nullptr;
+    int8_t *hq = Hq ? Hq : reinterpret_cast<int8_t *>(base + w.hq);
+    float *dhb = dh ? dh : reinterpret_cast<float *>(base + w.dh);
+    float *dz = reinterpret_cast<float *>(base + w.dz);
+    const int m = (int)M, k = (int)K, f = (int)F, n = (int)N;
+
+    hipError_t e = bl::launch_bitlinear(Xq, d, m, Wg, gamma_g, f, k, G, nullptr, s);
+    if (e == hipSuccess && Wu)
+        e = bl::launch_bitlinear(Xq, d, m, Wu, gamma_u, f, k, U, nullptr, s);
+    if (e == hipSuccess)
+        e = bl::launch_ffn_tail(G, U, norm_w, eps, m, f, hq, dhb, dz, s);
+    if (e == hipSuccess && n > 0)
+        e = bl::launch_bitlinear(hq, dz, m, Wd, gamma_d, n, f, Y, nullptr, s);
+    return launched(e, name);
+}

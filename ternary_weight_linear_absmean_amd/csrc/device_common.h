@@ -1,0 +1,74 @@
+// device_common.h -- device helpers shared by the libbitlinear kernels.
+//
+// Packed weight format ("Microsoft BitNet 深度研究报告", §2 (2), 实际存储:
+// codes {0: 0, +1: 1, -1: 2}; technical-report copy, GPU端: four weights per
+// int8): byte b of a row holds weights 4b..4b+3, weight 4b+j in bits 2j..2j+1.
+// A little-endian dword therefore holds 16 consecutive weights k = 16t + j,
+// code j in bits 2j..2j+1.
+//
+// Unpacking.  (dw >> 2i) & 0x03030303 puts the codes of weights
+// {i, 4+i, 8+i, 12+i} (one per byte) into a dword.  v_perm_b32 then maps each
+// code byte to the int8 value {0, +1, -1} in one instruction, using the code
+// as a byte selector into a constant table.  The four value dwords come out
+// in "transposed" order: dword i holds weights i, 4+i, 8+i, 12+i.  The
+// activations are put into the same order once (transpose16 below, a 4x4
+// byte transpose of each 16-byte group), so that value dword i lines up with
+// activation dword i and a v_dot4_i32_i8 (or an int8 MFMA) sums the right
+// products.  A dot product does not depend on the order of its terms, so
+// this reordering leaves every int32 sum exact and unchanged.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// v_perm_b32 semantics: the result byte i is selected by byte i of `sel`
+// from the 8 bytes {hi:lo} (selector 0..3 -> bytes of lo, 4..7 -> bytes of
+// hi, 8 -> bit 15 of lo replicated, 12 -> 0x00, >= 13 -> 0xFF).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Code selectors 0,1,2(,3) -> bytes of lo = {0x00, 0x01, 0xFF, 0x00}.
+constexpr uint32_t kLutLo0 = 0x00FF0100u;
+// Code selectors 0,4,8(,12) after masking with 0x0C: 0 -> lo byte 0 = 0x00,
+// 4 -> hi byte 0 = 0x01, 8 -> sign of lo byte 1 (0x80) = 0xFF, 12 -> 0x00.
+constexpr uint32_t kLutHi1 = 0x00000001u;
+constexpr uint32_t kLutLo1 = 0x00008000u;
+
+// 16 codes (one dword) -> four int8x4 value dwords, transposed order.
+__device__ __forceinline__ void unpack16(uint32_t dw, uint32_t &v0, uint32_t &v1,
+                                         uint32_t &v2, uint32_t &v3) {
+    const uint32_t dw4 = dw >> 4;
+    v0 = perm(0u, kLutLo0, dw & 0x03030303u);
+    v1 = perm(kLutHi1, kLutLo1, dw & 0x0C0C0C0Cu);
+    v2 = perm(0u, kLutLo0, dw4 & 0x03030303u);
+    v3 = perm(kLutHi1, kLutLo1, dw4 & 0x0C0C0C0Cu);
+}
+
+// 4x4 byte transpose of a 16-byte group: out dword i = bytes i of in dwords
+// 0..3, i.e. elements {i, 4+i, 8+i, 12+i}.
+__device__ __forceinline__ uint4 transpose16(uint4 v) {
+    const uint32_t lo01 = perm(v.y, v.x, 0x05010400u);  // x0 y0 x1 y1
+    const uint32_t hi01 = perm(v.y, v.x, 0x07030602u);  // x2 y2 x3 y3
+    const uint32_t lo23 = perm(v.w, v.z, 0x05010400u);  // z0 w0 z1 w1
+    const uint32_t hi23 = perm(v.w, v.z, 0x07030602u);  // z2 w2 z3 w3
+    uint4 o;
+    o.x = perm(lo23, lo01, 0x05040100u);                 // x0 y0 z0 w0
+    o.y = perm(lo23, lo01, 0x07060302u);                 // x1 y1 z1 w1
+    o.z = perm(hi23, hi01, 0x05040100u);                 // x2 y2 z2 w2
+    o.w = perm(hi23, hi01, 0x07060302u);                 // x3 y3 z3 w3
+    return o;
+}
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// fp32 rescale of an exact int32 sum: fl(float(acc) * c), c = fl(gamma * d).
+__device__ __forceinline__ float rescale(int32_t acc, float c) {
+    return __fmul_rn((float)acc, c);
+}
+
+}  // namespace bl

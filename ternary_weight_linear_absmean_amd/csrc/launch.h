@@ -1,0 +1,45 @@
+// launch.h -- internal kernel launchers of libbitlinear (not part of the ABI).
+// Callers have validated every argument; launchers only enqueue work on the
+// given stream and return the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bl {
+
+// Offline weight path: fp64 row sums of |W| into `rowsum` [N], gamma, packing.
+hipError_t launch_quant_weight(const float *W, int64_t N, int64_t K, uint8_t *Wp,
+                               float *gamma, double *rowsum, hipStream_t s);
+
+// Per-token absmax int8 quantisation; dtype 0 = fp32, 1 = bf16.
+hipError_t launch_quant_act(const void *X, int dtype, int64_t M, int64_t K,
+                            int8_t *Xq, float *d, hipStream_t s);
+
+// Y = float(acc) * fl(gamma * d[m]), acc = Xq . unpack(Wp)^T.  VALU kernel
+// (v_dot4) for a handful of tokens.
+hipError_t launch_gemv(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
+                       const float *gamma, int N, int K, float *Y, int32_t *acc,
+                       hipStream_t s);
+
+// Same product on int8 MFMA tiles, any M.
+hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
+                       const float *gamma, int N, int K, float *Y, int32_t *acc,
+                       hipStream_t s);
+
+// Largest M the VALU kernel takes in one pass over the weights.
+constexpr int kGemvMaxTokens = 8;
+
+// Picks the VALU kernel for M <= kGemvMaxTokens and MFMA otherwise.
+hipError_t launch_bitlinear(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
+                            const float *gamma, int N, int K, float *Y, int32_t *acc,
+                            hipStream_t s);
+
+// FFN tail on fp32 G, U [M][F]: H = relu(G)^2 * U, Hq / dh = absmax int8 of
+// H * g, dz = dh / rms(H).  U == NULL: ungated; norm_w == NULL: unit gain.
+hipError_t launch_ffn_tail(const float *G, const float *U, const float *norm_w,
+                           float eps, int M, int F, int8_t *Hq, float *dh, float *dz,
+                           hipStream_t s);
+
+}  // namespace bl

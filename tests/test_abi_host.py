@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI (CPU only, no GPU needed).
+
+The library must load, export every function include/bitlinear.h declares,
+and reject bad arguments with the documented status before it touches a
+device: every call below fails validation (or is an empty no-op), so no
+kernel is launched and no device memory is read.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_linear_absmean_amd as bl
+from ternary_weight_linear_absmean_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WS = 0, 1, 2, 3, 4, 5
+
+# fake, never-dereferenced addresses: validation fails before any use
+A16 = ctypes.c_void_p(0x10000)
+A4 = ctypes.c_void_p(0x10004)
+A1 = ctypes.c_void_p(0x10001)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bl.load()
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("quant_weight_absmean_pack", "quant_act_absmax_i8", "bitlinear_gemv",
+              "bitlinear_gemm", "bitlinear_ffn_relu2"):
+        assert n in names
+    assert sorted(names) == sorted(_native.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.bl_abi_version() == 1
+    for code, name in _native.STATUS.items():
+        assert lib.bl_status_string(code).decode() == name
+    assert lib.bl_status_string(99).decode() == "BL_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(lib):
+    assert lib.bl_workspace_bytes(bl.BL_OP_QUANT_WEIGHT, 0, 6912, 2560, 0) == 6912 * 8
+    assert lib.bl_workspace_bytes(bl.BL_OP_QUANT_WEIGHT, 0, 7, 2560, 0) == 256
+    M, F = 2048, 6912
+    ws = lib.bl_workspace_bytes(bl.BL_OP_FFN_RELU2, M, 2560, 2560, F)
+    assert ws >= M * F * (4 + 4 + 1) + 2 * M * 4
+    assert ws % 256 == 0
+    assert lib.bl_workspace_bytes(99, 1, 1, 1, 1) == 0
+
+
+def _err(lib):
+    return lib.bl_last_error().decode()
+
+
+def test_product_validation(lib):
+    for fn in (lib.bitlinear_gemv, lib.bitlinear_gemm):
+        # negative and unsupported sizes
+        assert fn(A16, A4, -1, A16, A4, 8, 64, A4, None, None) == SHAPE
+        assert "negative" in _err(lib)
+        assert fn(A16, A4, 1, A16, A4, 8, 96, A4, None, None) == SHAPE       # K % 64
+        assert fn(A16, A4, 1, A16, A4, 8, 2 * bl.BL_MAX_K, A4, None, None) == SHAPE
+        # empty problems are no-ops, even with NULL pointers
+        assert fn(None, None, 0, None, None, 8, 64, None, None, None) == OK
+        assert fn(None, None, 3, None, None, 0, 64, None, None, None) == OK
+        # NULL and misaligned pointers
+        assert fn(None, A4, 1, A16, A4, 8, 64, A4, None, None) == NULL
+        assert fn(A16, A4, 1, A16, None, 8, 64, A4, None, None) == NULL
+        assert fn(A1, A4, 1, A16, A4, 8, 64, A4, None, None) == ALIGN
+        assert fn(A16, A4, 1, A4, A4, 8, 64, A4, None, None) == ALIGN
+        assert fn(A16, A1, 1, A16, A4, 8, 64, A4, None, None) == ALIGN
+        assert fn(A16, A4, 1, A16, A4, 8, 64, A4, A1, None) == ALIGN
+    # the decode call takes at most 64 tokens
+    assert lib.bitlinear_gemv(A16, A4, 65, A16, A4, 8, 64, A4, None, None) == SHAPE
+
+
+def test_quant_validation(lib):
+    f = lib.quant_weight_absmean_pack
+    assert f(A16, 4, 6, A16, A4, A16, 1 << 20, None) == SHAPE            # K % 4
+    assert f(A16, -1, 8, A16, A4, A16, 1 << 20, None) == SHAPE
+    assert f(A16, 4, 8, A16, None, A16, 1 << 20, None) == NULL
+    assert f(None, 4, 8, A16, A4, A16, 1 << 20, None) == NULL
+    assert f(A4, 4, 8, A16, A4, A16, 1 << 20, None) == ALIGN
+    assert f(A16, 4, 8, A16, A4, A16, 8, None) == WS                      # needs 4 * 8
+    assert f(A16, 4, 8, A16, A4, None, 1 << 20, None) == WS
+    g = lib.quant_act_absmax_i8
+    assert g(A16, 0, -1, 8, A16, A4, None) == SHAPE
+    assert g(A16, 7, 1, 8, A16, A4, None) == DTYPE
+    assert g(None, 0, 0, 8, None, None, None) == OK
+    assert g(None, 0, 1, 8, A16, A4, None) == NULL
+    assert g(A4, 1, 1, 8, A16, A4, None) == ALIGN
+
+
+def test_ffn_validation(lib):
+    f = lib.bitlinear_ffn_relu2
+    big = 1 << 40
+    args = dict(Xq=A16, d=A4, M=2, K=64, F=128, Wg=A16, gg=A4, Wu=A16, gu=A4, nw=None,
+                eps=1e-5, Wd=A16, gd=A4, N=64, Y=A4, Hq=None, dh=None, ws=A16, wsb=big, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["Xq"], a["d"], a["M"], a["K"], a["F"], a["Wg"], a["gg"], a["Wu"], a["gu"],
+                 a["nw"], ctypes.c_float(a["eps"]), a["Wd"], a["gd"], a["N"], a["Y"], a["Hq"],
+                 a["dh"], a["ws"], a["wsb"], a["s"])
+
+    assert call(F=100) == SHAPE
+    assert call(K=-64) == SHAPE
+    assert call(eps=-1.0) == SHAPE
+    assert call(M=0, Xq=None, d=None) == OK
+    assert call(Wg=None) == NULL
+    assert call(Wu=A16, gu=None) == NULL
+    assert call(Hq=A4) == ALIGN
+    assert call(nw=A4) == ALIGN
+    assert call(wsb=16) == WS
+    assert call(ws=None) == WS
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        bl.quant_act_absmax_i8(torch.zeros(2, 64))

@@ -41,7 +41,7 @@ MUTANTS = [
     ("ffn_drops_gate", "float h = Wu ? r2 * U[m * F + f] : r2;", "float h = r2;"),
     ("ffn_relu_is_abs", "float r = G[m * F + f] > 0.0f ? G[m * F + f] : 0.0f;",
      "float r = fabsf(G[m * F + f]);"),
-    ("ffn_rms_multiplies", "* (double)dh[m] / rms[m];", "* (double)dh[m] * rms[m];"),
+    ("ffn_rms_multiplies", "(double)dh[m] / rms[m] : 0.0;", "(double)dh[m] * rms[m] : 0.0;"),
     ("ffn_rms_no_mean", "sqrt(ss / (double)F + (double)eps)", "sqrt(ss + (double)eps)"),
     ("ffn_gain_dropped", "float z = norm_w ? h * norm_w[f] : h;", "float z = h;"),
 ]

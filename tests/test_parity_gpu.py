@@ -1,0 +1,288 @@
+"""GPU parity: libbitlinear (through its C ABI) against the CPU oracle.
+
+Bar: every integer result (packed weights, gamma's bits, int8 activations and
+their scales, int32 accumulators, the FFN's int8 intermediate and its scale)
+is bit-exact; every fp32 output is within 1e-3 relative of the oracle's fp64
+value, element by element.  Inputs are the seeded synthetic workloads of
+workloads.py, at small sizes that span several tiles with ragged tails, and at
+the full 2B-class shapes (all outputs for the decode shapes; sampled token
+rows, which the oracle computes row by row, for prefill).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-3          # fp32 outputs against the oracle's fp64 values
+CANARY = -12345.678  # fills guard bands after every output
+
+
+def _f32_bits(x):
+    return np.asarray(x, dtype=np.float32).view(np.uint32)
+
+
+def _gpu_weight(bl, W):
+    Wp, g = bl.quant_weight_absmean_pack(W.cuda())
+    torch.cuda.synchronize()
+    return Wp, g
+
+
+def _ref_act(X):
+    if X.dtype == torch.bfloat16:
+        x32 = oracle.bf16_to_f32(workloads.bf16_bits(X))
+    else:
+        x32 = X.numpy()
+    return oracle.quant_act(x32)
+
+
+def _assert_close(Y, ref, rtol=RTOL):
+    Y = np.asarray(Y, dtype=np.float64)
+    err = np.abs(Y - ref)
+    bad = err > rtol * np.abs(ref)
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} outside rel {rtol}; "
+                           f"worst {np.max(err / np.maximum(np.abs(ref), 1e-300)):.3e}")
+
+
+def _guarded(shape, dtype, fill):
+    """An output tensor followed by a guard band; returns (view, guard)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    buf = torch.full((n + 256,), fill, dtype=dtype, device="cuda")
+    return buf[:n].view(*shape), buf[n:]
+
+
+# ---------------------------------------------------------------- weights
+@pytest.mark.parametrize("N,K,seed", [(256, 256, 0), (67, 260, 1), (640, 2560, 2),
+                                      (6912, 2560, 3), (2560, 6912, 4), (1, 4, 5)])
+def test_quant_weight_bit_exact(gpu, N, K, seed):
+    W = workloads.weight(workloads.generator(seed), N, K)
+    Wp, g = _gpu_weight(gpu, W)
+    Wp_ref, g_ref = oracle.quantize_weight(W.numpy())
+    assert _f32_bits(g.cpu().numpy()[0]) == _f32_bits(g_ref)
+    assert np.array_equal(Wp.cpu().numpy(), Wp_ref)
+
+
+def test_quant_weight_golden_and_ties(gpu):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "handworked.json")) as f:
+        cases = json.load(f)["weights"]
+    for c in cases:
+        W = torch.tensor(c["W"], dtype=torch.float32)
+        Wp, g = _gpu_weight(gpu, W)
+        assert g.item() == c["gamma"], c["derivation"]
+        assert Wp.cpu().tolist() == c["Wp"], c["derivation"]
+    # constant magnitude with random signs: gamma == |w|, Wq == sign
+    s = torch.randint(0, 2, (96, 128), generator=workloads.generator(8)).float() * 2 - 1
+    Wp, g = _gpu_weight(gpu, s * 0.0173)
+    assert g.item() == np.float32(0.0173)
+    assert np.array_equal(oracle.unpack(Wp.cpu().numpy(), 128), s.numpy().astype(np.int8))
+
+
+def test_quant_weight_empty(gpu):
+    g = torch.full((1,), 7.0, device="cuda")
+    for N, K in ((0, 64), (5, 0)):
+        W = torch.zeros(N, K, device="cuda")
+        Wp = torch.zeros(N, K // 4, dtype=torch.uint8, device="cuda")
+        gpu.quant_weight_absmean_pack(W, Wp=Wp, gamma=g)
+        torch.cuda.synchronize()
+        assert g.item() == 0.0
+
+
+# ------------------------------------------------------------ activations
+@pytest.mark.parametrize("M,K,dtype,seed", [
+    (4, 256, torch.float32, 0), (1, 2560, torch.bfloat16, 1), (1, 6912, torch.bfloat16, 2),
+    (64, 6912, torch.bfloat16, 3), (2048, 2560, torch.bfloat16, 4), (3, 257, torch.float32, 5),
+    (5, 260, torch.bfloat16, 6), (2, 1, torch.float32, 7)])
+def test_quant_act_bit_exact(gpu, M, K, dtype, seed):
+    X = workloads.activations(workloads.generator(seed), M, K, dtype=dtype)
+    if M > 1:
+        X[1] = 0                       # an all-zero token
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    Xq_ref, d_ref = _ref_act(X)
+    assert np.array_equal(Xq.cpu().numpy(), Xq_ref)
+    assert np.array_equal(_f32_bits(d.cpu().numpy()), _f32_bits(d_ref))
+
+
+def test_quant_act_golden(gpu):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "handworked.json")) as f:
+        cases = json.load(f)["activations"]
+    for c in cases:
+        Xq, d = gpu.quant_act_absmax_i8(torch.tensor(c["X"], dtype=torch.float32).cuda())
+        assert Xq.cpu().tolist() == c["Xq"], c["derivation"]
+        assert d.cpu().tolist() == c["d"], c["derivation"]
+
+
+# ------------------------------------------------------------------ products
+def _product_case(gpu, call, M, K, N, seed, dtype=torch.bfloat16):
+    W, X = workloads.bitlinear_problem(seed, M, K, N, dtype=dtype)
+    Wp, g = _gpu_weight(gpu, W)
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    Y, Yguard = _guarded((M, N), torch.float32, CANARY)
+    acc, Aguard = _guarded((M, N), torch.int32, -7)
+    getattr(gpu, call)(Xq, d, Wp, g, Y=Y, acc=acc)
+    torch.cuda.synchronize()
+    assert torch.all(Yguard == CANARY) and torch.all(Aguard == -7), "write past the output"
+    Xq_ref, d_ref = _ref_act(X)
+    Wp_ref, g_ref = oracle.quantize_weight(W.numpy())
+    acc_ref, Y_ref = oracle.bitlinear(Xq_ref, d_ref, Wp_ref, g_ref, K)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    _assert_close(Y.cpu().numpy(), Y_ref)
+    return Y, acc
+
+
+@pytest.mark.parametrize("shape", workloads.DECODE_SHAPES, ids=lambda s: s.name)
+def test_gemv_decode_shapes(gpu, shape):
+    _product_case(gpu, "bitlinear_gemv", 1, shape.K, shape.N, 10 + shape.N)
+
+
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8, 9, 13, 32, 64])
+def test_gemv_token_counts(gpu, M):
+    _product_case(gpu, "bitlinear_gemv", M, 2560, 640, 100 + M)
+
+
+@pytest.mark.parametrize("M", workloads.BATCHED_M)
+@pytest.mark.parametrize("shape", workloads.BATCHED_SHAPES, ids=lambda s: s.name)
+def test_gemv_batched_decode(gpu, M, shape):
+    _product_case(gpu, "bitlinear_gemv", M, shape.K, shape.N, 200 + M)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 1), (1, 64, 7), (3, 320, 641), (1, 6912, 97),
+                                   (7, 4096, 65), (1, 25600, 33), (8, 12288, 50),
+                                   (1, 131072, 9)])
+def test_gemv_ragged(gpu, M, K, N):
+    _product_case(gpu, "bitlinear_gemv", M, K, N, 300 + N)
+
+
+def test_tiny_config(gpu):
+    t = workloads.TINY
+    for call in ("bitlinear_gemv", "bitlinear_gemm"):
+        _product_case(gpu, call, t["M"], t["K"], t["N"], t["seed"], dtype=t["dtype"])
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 1), (130, 192, 131), (129, 2560, 257),
+                                   (256, 640, 384), (17, 6912, 100), (64, 2560, 640)])
+def test_gemm_ragged(gpu, M, K, N):
+    _product_case(gpu, "bitlinear_gemm", M, K, N, 400 + M)
+
+
+def test_gemm_prefill_full_size_sampled_rows(gpu):
+    """M = 2048, K = 2560 -> N = 6912 as timed; the oracle recomputes 24
+    sampled token rows (first, last, random) in full."""
+    p = workloads.PREFILL
+    M, K, N = p["M"], p["K"], p["F"]
+    W, X = workloads.bitlinear_problem(p["seed"], M, K, N)
+    Wp, g = _gpu_weight(gpu, W)
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    Y, acc = gpu.bitlinear_gemm(Xq, d, Wp, g, want_acc=True)
+    torch.cuda.synchronize()
+    Xq_ref, d_ref = _ref_act(X)
+    assert np.array_equal(Xq.cpu().numpy(), Xq_ref)
+    Wp_ref, g_ref = oracle.quantize_weight(W.numpy())
+    assert np.array_equal(Wp.cpu().numpy(), Wp_ref)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, M - 1],
+                                     np.random.default_rng(0).integers(0, M, 19)]))
+    acc_ref, Y_ref = oracle.bitlinear(Xq_ref[rows], d_ref[rows], Wp_ref, g_ref, K)
+    assert np.array_equal(acc.cpu().numpy()[rows], acc_ref)
+    _assert_close(Y.cpu().numpy()[rows], Y_ref)
+
+
+def test_gemv_equals_gemm(gpu):
+    """Both kernels give identical bits for every M the decode call takes."""
+    W, X = workloads.bitlinear_problem(31, 64, 2560, 1000)
+    Wp, g = _gpu_weight(gpu, W)
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    for M in (1, 2, 5, 8, 9, 64):
+        Y1, a1 = gpu.bitlinear_gemv(Xq[:M], d[:M], Wp, g, want_acc=True)
+        Y2, a2 = gpu.bitlinear_gemm(Xq[:M], d[:M], Wp, g, want_acc=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a1, a2) and torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
+
+
+def test_determinism(gpu):
+    W, X = workloads.bitlinear_problem(32, 300, 2560, 700)
+    Wp, g = _gpu_weight(gpu, W)
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    outs = [gpu.bitlinear_gemm(Xq, d, Wp, g) for _ in range(2)]
+    outs += [gpu.bitlinear_gemv(Xq[:8], d[:8], Wp, g) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[2], outs[3])
+
+
+def test_empty_products(gpu):
+    Xq = torch.zeros(0, 64, dtype=torch.int8, device="cuda")
+    d = torch.zeros(0, device="cuda")
+    Wp = torch.zeros(5, 16, dtype=torch.uint8, device="cuda")
+    g = torch.ones(1, device="cuda")
+    assert gpu.bitlinear_gemm(Xq, d, Wp, g).shape == (0, 5)
+    assert gpu.bitlinear_gemv(Xq, d, Wp, g).shape == (0, 5)
+
+
+# ------------------------------------------------------------------------ FFN
+def _ffn_case(gpu, M, K, F, N, seed, gated=True, gain=True, eps=1e-5, rows=None):
+    Wg, Wu, Wd, X = workloads.ffn_problem(seed, M, K, F, N)
+    Wgp, gg = _gpu_weight(gpu, Wg)
+    Wup, gu = _gpu_weight(gpu, Wu)
+    Wdp, gd = _gpu_weight(gpu, Wd)
+    nw = None
+    if gain:
+        nw = 1.0 + 0.5 * torch.randn(F, generator=workloads.generator(seed + 99))
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    Y, Hq, dh = gpu.bitlinear_ffn_relu2(Xq, d, Wgp, gg, Wup if gated else None,
+                                        gu if gated else None, Wdp, gd,
+                                        norm_w=nw.cuda() if gain else None, eps=eps,
+                                        want_debug=True)
+    torch.cuda.synchronize()
+    Xq_ref, d_ref = _ref_act(X)
+    if rows is None:
+        rows = np.arange(M)
+    ref = oracle.ffn_relu2(Xq_ref[rows], d_ref[rows], Wgp.cpu().numpy(), gg.item(),
+                           Wup.cpu().numpy() if gated else None, gu.item(),
+                           nw.numpy() if gain else None, eps, Wdp.cpu().numpy(), gd.item(),
+                           K, F, N)
+    assert np.array_equal(Hq.cpu().numpy()[rows], ref["Hq"])
+    assert np.array_equal(_f32_bits(dh.cpu().numpy()[rows]), _f32_bits(ref["dh"]))
+    _assert_close(Y.cpu().numpy()[rows], ref["Y"])
+
+
+@pytest.mark.parametrize("gated,gain", [(True, True), (True, False), (False, True)])
+def test_ffn_tiny(gpu, gated, gain):
+    _ffn_case(gpu, 4, 256, 512, 256, 40, gated=gated, gain=gain)
+
+
+@pytest.mark.parametrize("M", [1, 3, 37, 130])
+def test_ffn_token_counts(gpu, M):
+    _ffn_case(gpu, M, 320, 384, 200, 50 + M)
+
+
+def test_ffn_decode_shape(gpu):
+    _ffn_case(gpu, 1, 2560, 6912, 2560, 60)
+
+
+def test_ffn_prefill_full_size_sampled_rows(gpu):
+    p = workloads.PREFILL
+    rows = np.unique(np.concatenate([[0, p["M"] - 1],
+                                     np.random.default_rng(1).integers(0, p["M"], 10)]))
+    _ffn_case(gpu, p["M"], p["K"], p["F"], p["N"], p["seed"], rows=rows)
+
+
+def test_ffn_zero_token(gpu):
+    """An all-zero token gives zero codes, dh = 0 and a zero output row."""
+    M, K, F, N = 3, 128, 256, 64
+    Wg, Wu, Wd, X = workloads.ffn_problem(70, M, K, F, N)
+    Wgp, gg = _gpu_weight(gpu, Wg)
+    Wup, gu = _gpu_weight(gpu, Wu)
+    Wdp, gd = _gpu_weight(gpu, Wd)
+    X[1] = 0
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    Y, Hq, dh = gpu.bitlinear_ffn_relu2(Xq, d, Wgp, gg, Wup, gu, Wdp, gd, want_debug=True)
+    torch.cuda.synchronize()
+    assert dh[1].item() == 0 and not Hq[1].any() and not Y[1].any()
+    assert math.isfinite(Y.abs().max().item())
