@@ -68,40 +68,58 @@ def decode_setup(bl, torch, workloads):
     return sets, reps
 
 
-def decode_step(bl, sets, r, ev=None):
-    for j, p in enumerate(sets):
+def decode_step(bl, sets, r):
+    for p in sets:
         bl.quant_act_absmax_i8(p["X"], Xq=p["Xq"], d=p["d"])
-        if ev is not None:
-            ev[j][0].record()
         bl.bitlinear_gemv(p["Xq"], p["d"], p["Wp"][r], p["g"], Y=p["Y"])
-        if ev is not None:
-            ev[j][1].record()
 
 
 def bench_decode(bl, torch, workloads, steps, warmup):
+    """Step time from HIP-graph replays (one graph per weight copy, so the
+    host issues one launch per step), then the GEMV kernel's own duration
+    from event pairs around eager launches queued behind a sleep kernel (the
+    queue is full when they run, so no host gap enters the pairs)."""
     sets, reps = decode_setup(bl, torch, workloads)
-    for i in range(warmup):
+    for i in range(2 * reps):
         decode_step(bl, sets, i % reps)
     torch.cuda.synchronize()
-    # pass 1: the step as a whole
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for r in range(reps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                decode_step(bl, sets, r)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % reps].replay()
+    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        decode_step(bl, sets, (warmup + i) % reps)
+        graphs[(warmup + i) % reps].replay()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1)
-    # pass 2: the GEMV launches bracketed one by one on the same stream
+
+    # kernel durations: 3 queue packets per GEMV, kept well under the queue depth
+    per_pass = 48
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in sets]
-           for _ in range(steps)]
+           for _ in range(per_pass)]
+    torch.cuda._sleep(200_000_000)
+    for i in range(per_pass):
+        for j, p in enumerate(sets):
+            evs[i][j][0].record()
+            bl.bitlinear_gemv(p["Xq"], p["d"], p["Wp"][i % reps], p["g"], Y=p["Y"])
+            evs[i][j][1].record()
     torch.cuda.synchronize()
-    for i in range(steps):
-        decode_step(bl, sets, (warmup + steps + i) % reps, ev=evs[i])
-    torch.cuda.synchronize()
-    per_shape_us = [1000.0 * sum(evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps))
-                    / steps for j in range(len(sets))]
+    per_shape_us = [1000.0 * sum(evs[i][j][0].elapsed_time(evs[i][j][1])
+                                 for i in range(per_pass)) / per_pass
+                    for j in range(len(sets))]
     step_bytes = sum(gemv_bytes(1, p["shape"].K, p["shape"].N) for p in sets)
     shapes = []
     for p, us in zip(sets, per_shape_us):

@@ -27,6 +27,35 @@ constexpr int kUnitsInFlight = 4;           // 16-byte loads issued before use
 constexpr int kXBytes = 64 * 1024;          // LDS budget for staged activations
 
 template <int L, int MT>
+__device__ __forceinline__ void dot_unit(const uint4 &w, const uint4 *xs, int gpc, int ul,
+                                         int (&acc)[MT]) {
+    const uint32_t dws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uint32_t v0, v1, v2, v3;
+        unpack16(dws[t], v0, v1, v2, v3);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint4 xv = xs[m * gpc + 4 * ul + t];
+            int a = acc[m];
+            a = dot4(v0, xv.x, a);
+            a = dot4(v1, xv.y, a);
+            a = dot4(v2, xv.z, a);
+            a = dot4(v3, xv.w, a);
+            acc[m] = a;
+        }
+    }
+}
+
+template <int L>
+__device__ __forceinline__ void load_units(uint4 (&w)[kUnitsInFlight], const uint4 *wrow, int u,
+                                           int ue) {
+#pragma unroll
+    for (int j = 0; j < kUnitsInFlight; ++j)
+        w[j] = wrow[min(u + j * L, ue - 1)];            // clamped: always in bounds
+}
+
+template <int L, int MT>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K, int KC,
@@ -41,6 +70,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int m0 = blockIdx.y * MT;
     const int mt = min(MT, M - m0);
     const int gpc = KC / 16;                           // 16-byte groups per staged row
+    // Rows past N read the last row (in bounds) and are never stored.
     const uint4 *wrow = reinterpret_cast<const uint4 *>(Wp + (size_t)min(row, N - 1) * (K / 4));
 
     int acc[MT];
@@ -49,6 +79,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 
     for (int kc0 = 0; kc0 < K; kc0 += KC) {
         const int kc = min(KC, K - kc0);
+        const int ub = kc0 / 64;
+        const int ue = ub + kc / 64;
+        // The first weight loads do not depend on the activations: issue them
+        // before staging, so the two memory latencies overlap.
+        uint4 w[kUnitsInFlight];
+        load_units<L>(w, wrow, ub + s, ue);
         const int groups = kc / 16;
         __syncthreads();                               // previous chunk consumed
         for (int i = tid; i < mt * groups; i += kThreads) {
@@ -58,36 +94,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
             xs[m * gpc + g] = transpose16(v);
         }
         __syncthreads();
-        if (row < N) {
-            const int ub = kc0 / 64;
-            const int ue = ub + kc / 64;
-            for (int u = ub + s; u < ue; u += L * kUnitsInFlight) {
-                uint4 w[kUnitsInFlight];
+        for (int u = ub + s; u < ue; u += L * kUnitsInFlight) {
+            // software pipeline: the next batch is in flight while this one computes
+            uint4 wn[kUnitsInFlight];
+            const int un = u + L * kUnitsInFlight;
+            if (un < ue)
+                load_units<L>(wn, wrow, un, ue);
 #pragma unroll
-                for (int j = 0; j < kUnitsInFlight; ++j)
-                    w[j] = wrow[min(u + j * L, ue - 1)];      // clamped: always in bounds
+            for (int j = 0; j < kUnitsInFlight; ++j)
+                if (u + j * L < ue)
+                    dot_unit<L, MT>(w[j], xs, gpc, u + j * L - ub, acc);
+            if (un < ue) {
 #pragma unroll
-                for (int j = 0; j < kUnitsInFlight; ++j) {
-                    const int ul = u + j * L - ub;
-                    if (u + j * L < ue) {
-                        const uint32_t dws[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            uint32_t v0, v1, v2, v3;
-                            unpack16(dws[t], v0, v1, v2, v3);
-#pragma unroll
-                            for (int m = 0; m < MT; ++m) {
-                                const uint4 xv = xs[m * gpc + 4 * ul + t];
-                                int a = acc[m];
-                                a = dot4(v0, xv.x, a);
-                                a = dot4(v1, xv.y, a);
-                                a = dot4(v2, xv.z, a);
-                                a = dot4(v3, xv.w, a);
-                                acc[m] = a;
-                            }
-                        }
-                    }
-                }
+                for (int j = 0; j < kUnitsInFlight; ++j) w[j] = wn[j];
             }
         }
     }
@@ -128,9 +147,16 @@ template <int MT>
 hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                     const float *gamma, int N, int K, float *Y, int32_t *acc, hipStream_t s) {
     const int U = K / 64;                               // 16-byte units per row
-    if (U >= 96) return launch_lm<64, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
-    if (U >= 48) return launch_lm<32, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
-    return launch_lm<16, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    int L = U >= 96 ? 64 : U >= 48 ? 32 : 16;
+#ifdef BL_GEMV_FORCE_L
+    L = BL_GEMV_FORCE_L;                                // tuning builds only
+#endif
+    switch (L) {
+    case 8: return launch_lm<8, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    case 16: return launch_lm<16, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    case 32: return launch_lm<32, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    default: return launch_lm<64, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    }
 }
 
 }  // namespace
