@@ -3,18 +3,16 @@
 // The technical-report copy (推理完满 / GPU端) describes the W1.58A8 kernel as
 // pack, store, load, unpack, compute over four ternary weights per int8.  At
 // M = 2048 the product is compute-bound, so on gfx950 the unpacked ternary
-// tile goes through v_mfma_i32_16x16x64_i8 with int32 accumulation: the
-// ternary values {-1, 0, +1} are exact int8 operands and every int32 sum is
-// exact.  The rescale Y = float(acc) * fl(gamma * d[m]) is applied in the
-// epilogue.
+// tile goes through int8 MFMA with int32 accumulation: the values
+// {-1, 0, +1} are exact int8 operands and every int32 sum is exact.  The
+// rescale Y = float(acc) * fl(gamma * d[m]) is applied in the epilogue.
+// Both operands use the same transposed order inside every 16-byte group
+// (see device_common.h), so each MFMA lane multiplies matching k.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of Y as a 2 x 2
-// grid of waves, each owning 64 x 64 = 4 x 4 MFMA blocks of 16 x 16.  Per
-// 64-wide k-step the activation tile (128 rows x 64 int8) and the packed
-// weight tile (128 rows x 16 bytes) are read from global memory; the
-// weights are unpacked (v_perm byte lookup) into int8 in LDS.  Both operands
-// use the same transposed order inside every 16-byte group (see
-// device_common.h), so each MFMA lane multiplies matching k.
+// Two kernels:
+//   gemm_kernel     M < 128: 128 x 128 tiles of v_mfma_i32_16x16x64_i8,
+//                   4 waves, single-buffered LDS (A transposed, B unpacked).
+//   gemm256_kernel  M >= 128: see below.
 #include "device_common.h"
 #include "launch.h"
 
@@ -116,6 +114,200 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Large-M kernel on v_mfma_i32_32x32x32_i8 (on gfx950 the 32x32x32 int8 form
+// sustains about twice the throughput of 16x16x64 in a plain MFMA loop).
+// Workgroup = WM x WN waves, each wave owns 128 x 64 of Y = 4 x 2 blocks of
+// 32 x 32 (128 int32 accumulators per lane); tile = 128 WM x 64 WN.
+//   <2, 4>: 256 x 256 tiles, 512 threads (wide N, e.g. K2560 -> N6912)
+//   <1, 2>: 128 x 128 tiles, 128 threads (narrow N, e.g. K6912 -> N2560,
+//           where 256 x 256 tiles would leave most CUs idle)
+// k-step 128: the activation tile (transposed 16-byte groups, see
+// device_common.h) and the packed weight tile (2-bit codes, 4x smaller than
+// int8) are staged in LDS, double-buffered, from registers loaded two
+// k-steps ahead; each wave unpacks its B operands (one v_perm per four
+// weights) right after reading the packed dwords from LDS.  One barrier per
+// k-step; __builtin_amdgcn_iglp_opt(1) asks the scheduler to interleave the
+// LDS reads with the MFMAs.  A K tail of 64 (K % 128 == 64) is one extra
+// half step.  Rows past M and columns past N read clamped (valid) addresses
+// and their outputs are never stored.
+//
+// Workgroup i runs M-tile i % m_tiles and N-tile i / m_tiles: workgroups are
+// dealt to the 8 XCDs round-robin, so with 8 M-tiles each XCD keeps one
+// M-tile of activations resident in its L2 while it streams packed weights.
+constexpr int BK2 = 128;
+constexpr int kAPitch = BK2 / 16 + 1;          // uint4 per A row (8 + 1 pad)
+constexpr int kBPitch = BK2 / 16 + 1;          // dwords per B column (8 + 1 pad)
+constexpr int MI2 = 4, NJ2 = 2;
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+template <int AG, int BG> struct Stage2 { uint4 a[AG]; uint4 b[BG]; };
+template <int AG, int BG> struct SrcPtr { const int8_t *a[AG]; const uint8_t *b[BG]; };
+
+// Per k-step a workgroup of T threads stages BM rows x 128 bytes of A (BM * 8
+// groups of 16 bytes, AG = BM * 8 / T per thread) and BN columns x 32 packed
+// bytes of B (BN * 2 groups of 16 bytes, BG = BN * 2 / T per thread).
+template <int BM, int BN, int T, int AG, int BG>
+__device__ __forceinline__ SrcPtr<AG, BG> src_ptrs(const int8_t *__restrict__ Xq,
+        const uint8_t *__restrict__ Wp, int M, int N, int K, int KB, int m_base, int n_base, int tid) {
+    SrcPtr<AG, BG> p;
+#pragma unroll
+    for (int i = 0; i < AG; ++i) {
+        const int idx = tid + T * i;
+        const int r = min(m_base + (idx >> 3), M - 1);
+        p.a[i] = Xq + (size_t)r * K + 16 * (idx & 7);
+    }
+#pragma unroll
+    for (int i = 0; i < BG; ++i) {
+        const int idx = tid + T * i;
+        const int gn = min(n_base + (idx >> 1), N - 1);
+        p.b[i] = Wp + (size_t)gn * KB + 16 * (idx & 1);
+    }
+    return p;
+}
+template <int AG, int BG>
+__device__ __forceinline__ void load_stage2(Stage2<AG, BG> &st, const SrcPtr<AG, BG> &sp, int k0) {
+#pragma unroll
+    for (int i = 0; i < AG; ++i) st.a[i] = *reinterpret_cast<const uint4 *>(sp.a[i] + k0);
+#pragma unroll
+    for (int i = 0; i < BG; ++i) st.b[i] = *reinterpret_cast<const uint4 *>(sp.b[i] + k0 / 4);
+}
+template <int T, int AG, int BG>
+__device__ __forceinline__ void store_stage2(const Stage2<AG, BG> &st, uint4 *As, uint32_t *Bs, int tid) {
+#pragma unroll
+    for (int i = 0; i < AG; ++i) {
+        const int idx = tid + T * i;
+        As[(idx >> 3) * kAPitch + (idx & 7)] = transpose16(st.a[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < BG; ++i) {
+        const int idx = tid + T * i;
+        uint32_t *b = Bs + (idx >> 1) * kBPitch + 4 * (idx & 1);
+        b[0] = st.b[i].x; b[1] = st.b[i].y; b[2] = st.b[i].z; b[3] = st.b[i].w;
+    }
+}
+
+template <int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
+    const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
+    const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
+    float *__restrict__ Y, int32_t *__restrict__ acc_out, int m_tiles) {
+    constexpr int BM2 = 128 * WM, BN2 = 64 * WN, kThreads2 = 64 * WM * WN;
+    constexpr int AG = BM2 * 8 / kThreads2, BG = BN2 * 2 / kThreads2;
+    constexpr int kStageA = BM2 * kAPitch, kStageB = BN2 * kBPitch;
+    __shared__ uint4 As[2 * kStageA];
+    __shared__ uint32_t Bs[2 * kStageB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int m_base = (blockIdx.x % m_tiles) * BM2;
+    const int n_base = (blockIdx.x / m_tiles) * BN2;
+    const int KB = K / 4;
+    const int KT = K / BK2;                    // full 128-wide steps
+    v16i acc[MI2][NJ2];
+#pragma unroll
+    for (int i = 0; i < MI2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ2; ++j) acc[i][j] = v16i{};
+    const SrcPtr<AG, BG> sp = src_ptrs<BM2, BN2, kThreads2, AG, BG>(Xq, Wp, M, N, K, KB, m_base, n_base, tid);
+    const int a_off = (wm * 128 + (lane & 31)) * kAPitch + (lane >> 5);
+    const int b_off = (wn * 64 + (lane & 31)) * kBPitch + (lane >> 5);
+    Stage2<AG, BG> s0, s1;
+    if (KT > 0) load_stage2(s0, sp, 0);
+    if (KT > 1) load_stage2(s1, sp, BK2);
+    if (KT > 0) store_stage2<kThreads2>(s0, As, Bs, tid);
+    __syncthreads();
+#define BL_STEP(KT_, MINE, NEXT)                                                              \
+    {                                                                                         \
+        const int kt_ = (KT_);                                                                \
+        if (kt_ + 2 < KT) load_stage2(MINE, sp, (kt_ + 2) * BK2);                             \
+        const int buf = kt_ & 1;                                                              \
+        __builtin_amdgcn_iglp_opt(1);                                                       \
+        const uint4 *A = As + buf * kStageA + a_off;                                          \
+        const uint32_t *B = Bs + buf * kStageB + b_off;                                       \
+        _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                       \
+            v4i bf[NJ2];                                                                      \
+            _Pragma("unroll") for (int j = 0; j < NJ2; ++j) {                                 \
+                uint4 v;                                                                      \
+                unpack16(B[j * 32 * kBPitch + 2 * h], v.x, v.y, v.z, v.w);                    \
+                bf[j] = as_v4i(v);                                                            \
+            }                                                                                 \
+            v4i af[MI2];                                                                      \
+            _Pragma("unroll") for (int i = 0; i < MI2; ++i)                                   \
+                af[i] = as_v4i(A[i * 32 * kAPitch + 2 * h]);                                  \
+            _Pragma("unroll") for (int i = 0; i < MI2; ++i)                                   \
+                _Pragma("unroll") for (int j = 0; j < NJ2; ++j)                               \
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0); \
+        }                                                                                     \
+        if (kt_ + 1 < KT) store_stage2<kThreads2>(NEXT, As + (buf ^ 1) * kStageA, Bs + (buf ^ 1) * kStageB, tid); \
+        __syncthreads();                                                                      \
+    }
+    int kt = 0;
+#pragma unroll 1
+    for (; kt + 2 <= KT; kt += 2) {
+        BL_STEP(kt, s0, s1)
+        BL_STEP(kt + 1, s1, s0)
+    }
+    if (kt < KT) BL_STEP(kt, s0, s1)
+#undef BL_STEP
+    // K % 128 == 64: one last 64-wide half step straight from global memory
+    if (K % BK2) {
+        const int k0 = KT * BK2;
+        Stage2<AG, BG> st;
+#pragma unroll
+        for (int i = 0; i < AG; ++i) {
+            const int idx = tid + kThreads2 * i;
+            st.a[i] = (idx & 7) < 4 ? *reinterpret_cast<const uint4 *>(sp.a[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < BG; ++i) {
+            const int idx = tid + kThreads2 * i;
+            st.b[i] = (idx & 1) == 0 ? *reinterpret_cast<const uint4 *>(sp.b[i] + k0 / 4) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        store_stage2<kThreads2>(st, As, Bs, tid);
+        __syncthreads();
+        const uint4 *A = As + a_off;
+        const uint32_t *B = Bs + b_off;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4i bf[NJ2];
+#pragma unroll
+            for (int j = 0; j < NJ2; ++j) {
+                uint4 v;
+                unpack16(B[j * 32 * kBPitch + 2 * h], v.x, v.y, v.z, v.w);
+                bf[j] = as_v4i(v);
+            }
+#pragma unroll
+            for (int i = 0; i < MI2; ++i) {
+                const v4i a = as_v4i(A[i * 32 * kAPitch + 2 * h]);
+#pragma unroll
+                for (int j = 0; j < NJ2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bf[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+
+    const float g = gamma[0];
+#pragma unroll
+    for (int i = 0; i < MI2; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = m_base + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (row >= M) continue;
+            const float c = __fmul_rn(g, d[row]);
+#pragma unroll
+            for (int j = 0; j < NJ2; ++j) {
+                const int col = n_base + wn * 64 + j * 32 + (lane & 31);
+                if (col < N) {
+                    const size_t o = (size_t)row * N + col;
+                    Y[o] = rescale(acc[i][j][r], c);
+                    if (acc_out) acc_out[o] = acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
@@ -123,6 +315,26 @@ hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *W
                        hipStream_t s) {
     if (M == 0 || N == 0)
         return hipSuccess;
+    if (M >= 128) {
+        int cfg = (N >= 4096 && M >= 256) ? 0 : 1;
+#ifdef BL_GEMM_CFG
+        cfg = BL_GEMM_CFG;                        // tuning builds only
+#endif
+        if (cfg == 0) {
+            const int m_tiles = (M + 255) / 256, n_tiles = (N + 255) / 256;
+            hipLaunchKernelGGL((gemm256_kernel<2, 4>), dim3(m_tiles * n_tiles), dim3(512), 0, s, Xq, d,
+                               M, Wp, gamma, N, K, Y, acc, m_tiles);
+        } else if (cfg == 1) {
+            const int m_tiles = (M + 127) / 128, n_tiles = (N + 127) / 128;
+            hipLaunchKernelGGL((gemm256_kernel<1, 2>), dim3(m_tiles * n_tiles), dim3(128), 0, s, Xq, d,
+                               M, Wp, gamma, N, K, Y, acc, m_tiles);
+        } else {
+            const int m_tiles = (M + 255) / 256, n_tiles = (N + 127) / 128;
+            hipLaunchKernelGGL((gemm256_kernel<2, 2>), dim3(m_tiles * n_tiles), dim3(256), 0, s, Xq, d,
+                               M, Wp, gamma, N, K, Y, acc, m_tiles);
+        }
+        return hipGetLastError();
+    }
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, Xq, d, M, Wp, gamma, N, K, Y, acc);
     return hipGetLastError();

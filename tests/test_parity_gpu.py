@@ -168,7 +168,8 @@ def test_tiny_config(gpu):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (130, 192, 131), (129, 2560, 257),
-                                   (256, 640, 384), (17, 6912, 100), (64, 2560, 640)])
+                                   (256, 640, 384), (17, 6912, 100), (64, 2560, 640),
+                                   (513, 128, 257), (300, 6912, 300), (1024, 64, 512)])
 def test_gemm_ragged(gpu, M, K, N):
     _product_case(gpu, "bitlinear_gemm", M, K, N, 400 + M)
 
