@@ -4,11 +4,14 @@
 
 A step is one decode pass over the four 2B-class BitLinear shapes (M = 1
 token, bf16 activations -> per-token int8 -> ternary GEMV -> fp32):
-K2560->N2560, K2560->N640, K2560->N6912, K6912->N2560.  Weights are rotated
-over enough distinct packed copies (> 2 x the 256 MB Infinity Cache) that
-every step reads its weights from HBM.  ``value`` is the GEMV algorithmic
-bytes moved per step (packed weights + int8 activations + fp32 outputs +
-scales) over the measured step time, in GB/s.
+K2560->N2560, K2560->N640, K2560->N6912, K6912->N2560, as one fused launch
+(bitlinear_gemv_fused) replayed from a HIP graph.  Weights are rotated over
+enough distinct packed copies (> 2 x the 256 MB Infinity Cache) that every
+step reads its weights from HBM.  ``value`` is the algorithmic bytes moved
+per step (packed weights + bf16 activations + fp32 outputs + gamma: 10,975,248
+B for the four shapes) over the
+measured step time, in GB/s.  The same step as separate quant + GEMV calls
+is reported as ``decode_unfused``.
 
 Also measured in the same run and reported beside it: the prefill GEMM
 (M = 2048, K2560->N6912, int8 TOPS against the int8 MFMA peak), the prefill
@@ -34,9 +37,10 @@ I8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
 COLD_BYTES = 600 * 2 ** 20     # > 2 x 256 MB Infinity Cache
 
 
-def gemv_bytes(M, K, N):
-    """Algorithmic bytes of one BitLinear: packed W + int8 X + fp32 Y + d + gamma."""
-    return N * K // 4 + M * K + 4 * M * N + 4 * M + 4
+def decode_bytes(K, N):
+    """Algorithmic bytes of one M = 1 BitLinear from bf16 activations: packed
+    2-bit W + bf16 X + fp32 Y + gamma."""
+    return N * K // 4 + 2 * K + 4 * N + 4
 
 
 def parse():
@@ -55,6 +59,7 @@ def decode_setup(bl, torch, workloads):
     shapes = workloads.DECODE_SHAPES
     per_step = sum(s.N * s.K // 4 for s in shapes)
     reps = max(2, math.ceil(COLD_BYTES / per_step))
+    reps = STEPS_PER_GRAPH * math.ceil(reps / STEPS_PER_GRAPH)
     sets = []
     for i, s in enumerate(shapes):
         W, X = workloads.bitlinear_problem(i, 1, s.K, s.N)
@@ -68,69 +73,97 @@ def decode_setup(bl, torch, workloads):
     return sets, reps
 
 
-def decode_step(bl, sets, r):
+def fused_step(bl, sets, r):
+    """One decode step: a single launch, act quant fused into the four GEMVs."""
+    bl.bitlinear_gemv_fused([dict(X=p["X"], Wp=p["Wp"][r], gamma=p["g"], Y=p["Y"])
+                             for p in sets])
+
+
+def unfused_step(bl, sets, r):
+    """The same step as two calls per shape (quant_act_absmax_i8 + bitlinear_gemv)."""
     for p in sets:
         bl.quant_act_absmax_i8(p["X"], Xq=p["Xq"], d=p["d"])
         bl.bitlinear_gemv(p["Xq"], p["d"], p["Wp"][r], p["g"], Y=p["Y"])
 
 
-def bench_decode(bl, torch, workloads, steps, warmup):
-    """Step time from HIP-graph replays (one graph per weight copy, so the
-    host issues one launch per step), then the GEMV kernel's own duration
-    from event pairs around eager launches queued behind a sleep kernel (the
-    queue is full when they run, so no host gap enters the pairs)."""
-    sets, reps = decode_setup(bl, torch, workloads)
-    for i in range(2 * reps):
-        decode_step(bl, sets, i % reps)
-    torch.cuda.synchronize()
+STEPS_PER_GRAPH = 10
+
+
+def capture(torch, fn, reps, per_graph):
+    """HIP graphs over the weight copies: graph i holds `per_graph` consecutive
+    steps (copies i*per_graph ...), plus one single-step graph per copy for
+    step counts that are not a multiple.  A graph only changes how the host
+    launches the steps, not the work each step does."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    graphs = []
+    multi, single = [], []
     with torch.cuda.stream(side):
+        for start in range(0, reps, per_graph):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for r in range(start, start + per_graph):
+                    fn(r)
+            multi.append(g)
         for r in range(reps):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=side):
-                decode_step(bl, sets, r)
-            graphs.append(g)
+                fn(r)
+            single.append(g)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    for i in range(warmup):
-        graphs[i % reps].replay()
+    return multi, single
+
+
+def replay_ms(torch, graphs, steps, warmup, per_graph):
+    """Replay exactly `steps` steps after `warmup` warm-up steps; returns ms."""
+    multi, single = graphs
+
+    def run(n, first):
+        done = 0
+        i = first
+        while n - done >= per_graph:
+            multi[i % len(multi)].replay()
+            done += per_graph
+            i += 1
+        while done < n:
+            single[(i * per_graph + done) % len(single)].replay()
+            done += 1
+        return i
+
+    nxt = run(warmup, 0)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for i in range(steps):
-        graphs[(warmup + i) % reps].replay()
+    run(steps, nxt)
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1)
+    return t0.elapsed_time(t1)
 
-    # kernel durations: 3 queue packets per GEMV, kept well under the queue depth
-    per_pass = 48
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in sets]
-           for _ in range(per_pass)]
-    torch.cuda._sleep(200_000_000)
-    for i in range(per_pass):
-        for j, p in enumerate(sets):
-            evs[i][j][0].record()
-            bl.bitlinear_gemv(p["Xq"], p["d"], p["Wp"][i % reps], p["g"], Y=p["Y"])
-            evs[i][j][1].record()
+
+def bench_decode(bl, torch, workloads, steps, warmup):
+    """The decode step replayed from HIP graphs over cold weight copies.  With
+    the fused call a step is exactly one kernel, so the event-timed region
+    over K steps gives that kernel's average launch duration (with the
+    dispatch gap between back-to-back kernels) directly."""
+    sets, reps = decode_setup(bl, torch, workloads)
+    for r in range(reps):
+        fused_step(bl, sets, r)
+        unfused_step(bl, sets, r)
     torch.cuda.synchronize()
-    per_shape_us = [1000.0 * sum(evs[i][j][0].elapsed_time(evs[i][j][1])
-                                 for i in range(per_pass)) / per_pass
-                    for j in range(len(sets))]
-    step_bytes = sum(gemv_bytes(1, p["shape"].K, p["shape"].N) for p in sets)
-    shapes = []
-    for p, us in zip(sets, per_shape_us):
-        b = gemv_bytes(1, p["shape"].K, p["shape"].N)
-        shapes.append(dict(shape=p["shape"].name, K=p["shape"].K, N=p["shape"].N,
-                           bytes=b, us=round(us, 3), GBs=round(b / us / 1e3, 1)))
-    kernel_us = sum(per_shape_us) / len(per_shape_us)
-    achieved = (step_bytes / len(sets)) / kernel_us / 1e3
-    return dict(ms_total=ms, ms_per_step=ms / steps, step_bytes=step_bytes,
-                value=step_bytes * steps / (ms * 1e-3) / 1e9, reps=reps,
-                kernel_us=kernel_us, achieved=achieved, shapes=shapes)
+    g_fused = capture(torch, lambda r: fused_step(bl, sets, r), reps, STEPS_PER_GRAPH)
+    ms = replay_ms(torch, g_fused, steps, warmup, STEPS_PER_GRAPH)
+    g_unfused = capture(torch, lambda r: unfused_step(bl, sets, r), reps, STEPS_PER_GRAPH)
+    ms_unfused = replay_ms(torch, g_unfused, steps, warmup, STEPS_PER_GRAPH)
+    # bf16 activations are read by the fused kernel (quantisation is fused)
+    step_bytes = sum(decode_bytes(p["shape"].K, p["shape"].N) for p in sets)
+    us = 1000.0 * ms / steps
+    return dict(ms_per_step=ms / steps, step_bytes=step_bytes,
+                value=step_bytes / us / 1e3, reps=reps, kernel_us=us,
+                achieved=step_bytes / us / 1e3,
+                unfused=dict(us_per_step=round(1000.0 * ms_unfused / steps, 3),
+                             GBs=round(step_bytes * steps / (ms_unfused * 1e-3) / 1e9, 1),
+                             launches_per_step=2 * len(sets)))
 
 
 def bench_gemm(bl, torch, workloads, steps, warmup):
@@ -190,7 +223,7 @@ def cpu_baseline(torch, workloads, seconds):
         W, X = workloads.bitlinear_problem(i, 1, s.K, s.N)
         Wp, g = oracle.quantize_weight(W.numpy())
         probs.append((s, Wp, g, workloads.bf16_bits(X)))
-    step_bytes = sum(gemv_bytes(1, s.K, s.N) for s, _, _, _ in probs)
+    step_bytes = sum(decode_bytes(s.K, s.N) for s, _, _, _ in probs)
     passes = 0
     t0 = time.perf_counter()
     while True:
@@ -233,9 +266,10 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": round(dec["achieved"], 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
-                           "kernel": "gemv_kernel (bitlinear_gemv, M=1)",
-                           "avg_launch_us": round(dec["kernel_us"], 3)}
-        out["decode_shapes"] = dec["shapes"]
+                           "kernel": "gemv_fused_kernel<1> (bitlinear_gemv_fused, 4 jobs, M=1)",
+                           "avg_launch_us": round(dec["kernel_us"], 3),
+                           "bytes_per_launch": dec["step_bytes"]}
+        out["decode_unfused"] = dec["unfused"]
         out["config"]["weight_copies"] = dec["reps"]
         out["config"]["step_bytes"] = dec["step_bytes"]
     if args.part in ("all", "gemm"):

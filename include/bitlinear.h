@@ -153,6 +153,46 @@ bl_status bitlinear_gemm(const int8_t *Xq, const float *d, int64_t M,
                          float *Y, int32_t *acc, void *stream);
 
 /* ------------------------------------------------------------------------
+ * bitlinear_gemv_fused -- decode step: per-token absmax int8 quantisation
+ * folded into the GEMV, for up to BL_MAX_JOBS independent BitLinears in one
+ * launch.  Each job is Y = BitLinear(X) with its own activations, weights
+ * and output, exactly as quant_act_absmax_i8 followed by bitlinear_gemv
+ * (same int8 codes, scales, int32 sums and fp32 Y, bit for bit); the
+ * quantisation is recomputed by every workgroup from X, so no intermediate
+ * round trip through memory or second launch is needed.
+ * [NEWS] 权重映射为三元值 (per-token absmax int8); [RPT] §2 (3) 查找表优化;
+ * [TR] GPU端 (load packed weights, unpack, compute).
+ *
+ *   jobs   in   HOST array of `count` bl_gemv_job (read before return; the
+ *               pointers inside are device pointers).
+ *   count       1 <= count <= BL_MAX_JOBS.
+ *   M           tokens, 1 <= M <= 8, shared by all jobs.
+ * Per job: X is [M][K] of `dtype` (BL_F32 / BL_BF16, 16-byte aligned),
+ * K % 64 == 0, 0 < K <= 16384, N >= 0, and T * K * (1 + element size) <=
+ * 131072 bytes of LDS staging, T = M rounded up to 1, 2, 4 or 8 (e.g. M = 1:
+ * K <= 16384; M = 8 bf16: K <= 5461); Wp [N][K/4] and gamma as for
+ * bitlinear_gemv; Y [M][N] fp32; Xq [M][K] int8 and d [M] fp32 are optional
+ * outputs (NULL = not written) holding the quantised activations.  Jobs
+ * may share X; no output may overlap another job's input or output.
+ */
+#define BL_MAX_JOBS 8
+
+typedef struct {
+    const void *X;
+    const uint8_t *Wp;
+    const float *gamma;
+    float *Y;
+    int8_t *Xq;
+    float *d;
+    int64_t N;
+    int64_t K;
+    int32_t dtype;
+    int32_t reserved;     /* must be 0 */
+} bl_gemv_job;
+
+bl_status bitlinear_gemv_fused(const bl_gemv_job *jobs, int count, int64_t M, void *stream);
+
+/* ------------------------------------------------------------------------
  * bitlinear_ffn_relu2 -- the feed-forward tail of a BitNet b1.58 block:
  * ReLU² (gated) + subln RMSNorm + int8 requantisation + down projection.
  * [NEWS] 权重映射为三元值 (ReLU² in place of SwiGLU; subln);

@@ -25,8 +25,17 @@ STATUS = {0: "BL_OK", 1: "BL_ERR_NULL", 2: "BL_ERR_SHAPE", 3: "BL_ERR_DTYPE",
           4: "BL_ERR_ALIGN", 5: "BL_ERR_WORKSPACE", 6: "BL_ERR_ARCH", 7: "BL_ERR_HIP"}
 
 EXPORTS = ["quant_weight_absmean_pack", "quant_act_absmax_i8", "bitlinear_gemv",
-           "bitlinear_gemm", "bitlinear_ffn_relu2", "bl_workspace_bytes",
-           "bl_status_string", "bl_last_error", "bl_abi_version"]
+           "bitlinear_gemm", "bitlinear_gemv_fused", "bitlinear_ffn_relu2",
+           "bl_workspace_bytes", "bl_status_string", "bl_last_error", "bl_abi_version"]
+BL_MAX_JOBS = 8
+
+
+class GemvJob(ctypes.Structure):
+    """bl_gemv_job (include/bitlinear.h)."""
+    _fields_ = [("X", ctypes.c_void_p), ("Wp", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("Xq", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 _lib = None
 _p = ctypes.c_void_p
@@ -58,6 +67,8 @@ def load():
         f = getattr(lib, name)
         f.restype = st
         f.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _p]
+    lib.bitlinear_gemv_fused.restype = st
+    lib.bitlinear_gemv_fused.argtypes = [ctypes.POINTER(GemvJob), ctypes.c_int, _i64, _p]
     lib.bitlinear_ffn_relu2.restype = st
     lib.bitlinear_ffn_relu2.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p,
                                         ctypes.c_float, _p, _p, _i64, _p, _p, _p, _p, _sz, _p]
@@ -169,6 +180,52 @@ def bitlinear_gemv(Xq, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=No
 def bitlinear_gemm(Xq, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=None):
     """Y [M, N] fp32 for any M on int8 MFMA; with want_acc also int32 acc."""
     return _product("bitlinear_gemm", Xq, d, Wp, gamma, Y, acc, want_acc, stream)
+
+
+def bitlinear_gemv_fused(jobs, stream=None):
+    """Fused decode step: each job is a dict with X ([M, K] fp32 / bf16), Wp,
+    gamma and optional Y, Xq, d (allocated when absent; Xq / d only when the
+    key is present with None meaning "allocate").  Returns the list of jobs
+    with their output tensors filled in."""
+    if not 1 <= len(jobs) <= BL_MAX_JOBS:
+        raise ValueError(f"1..{BL_MAX_JOBS} jobs")
+    arr = (GemvJob * len(jobs))()
+    M = None
+    out = []
+    for i, j in enumerate(jobs):
+        X = j["X"]
+        if X.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("X must be float32 or bfloat16")
+        _dev(X, X.dtype, "X")
+        _dev(j["Wp"], torch.uint8, "Wp")
+        _dev(j["gamma"], torch.float32, "gamma")
+        m, K = X.shape
+        if M is None:
+            M = m
+        elif m != M:
+            raise ValueError("all jobs must have the same number of tokens")
+        N = j["Wp"].shape[0]
+        if j["Wp"].shape[1] * 4 != K:
+            raise ValueError("Wp must be [N, K/4]")
+        dev = X.device
+        r = dict(j)
+        r["Y"] = _dev(j.get("Y"), torch.float32, "Y") if j.get("Y") is not None else \
+            torch.empty((M, N), dtype=torch.float32, device=dev)
+        if "Xq" in j:
+            r["Xq"] = j["Xq"] if j["Xq"] is not None else torch.empty((M, K), dtype=torch.int8,
+                                                                        device=dev)
+            _dev(r["Xq"], torch.int8, "Xq")
+        if "d" in j:
+            r["d"] = j["d"] if j["d"] is not None else torch.empty((M,), dtype=torch.float32,
+                                                                     device=dev)
+            _dev(r["d"], torch.float32, "d")
+        arr[i] = GemvJob(X.data_ptr(), j["Wp"].data_ptr(), j["gamma"].data_ptr(),
+                         r["Y"].data_ptr(), r["Xq"].data_ptr() if r.get("Xq") is not None else None,
+                         r["d"].data_ptr() if r.get("d") is not None else None, N, K,
+                         BL_BF16 if X.dtype == torch.bfloat16 else BL_F32, 0)
+        out.append(r)
+    _check("bitlinear_gemv_fused", load().bitlinear_gemv_fused(arr, len(jobs), M, _stream(stream)))
+    return out
 
 
 def bitlinear_ffn_relu2(Xq, d, Wg, gamma_g, Wu, gamma_u, Wd, gamma_d, norm_w=None, eps=1e-5,

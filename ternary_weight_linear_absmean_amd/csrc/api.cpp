@@ -234,6 +234,46 @@ BL_EXPORT bl_status bitlinear_gemm(const int8_t *Xq, const float *d, int64_t M, 
                     "bitlinear_gemm");
 }
 
+BL_EXPORT bl_status bitlinear_gemv_fused(const bl_gemv_job *jobs, int count, int64_t M,
+                                         void *stream) {
+    const char *name = "bitlinear_gemv_fused";
+    if (!jobs)
+        return fail(BL_ERR_NULL, "%s: jobs is NULL", name);
+    if (count < 1 || count > BL_MAX_JOBS)
+        return fail(BL_ERR_SHAPE, "%s: count=%d must be in [1, %d]", name, count, BL_MAX_JOBS);
+    if (M < 1 || M > bl::kGemvMaxTokens)
+        return fail(BL_ERR_SHAPE, "%s: M=%lld must be in [1, %d]", name, (long long)M,
+                    bl::kGemvMaxTokens);
+    bl::GemvJob gj[BL_MAX_JOBS];
+    for (int j = 0; j < count; ++j) {
+        const bl_gemv_job &b = jobs[j];
+        if (b.dtype != BL_F32 && b.dtype != BL_BF16)
+            return fail(BL_ERR_DTYPE, "%s: job %d: unknown dtype %d", name, j, (int)b.dtype);
+        const int esize = b.dtype == BL_F32 ? 4 : 2;
+        if (b.N < 0 || b.N > kI32Max || b.K <= 0 || b.K % 64 != 0 || b.K > 16384 ||
+            bl::fused_lds_bytes(bl::fused_tile((int)M), (int)b.K, esize) > bl::kFusedMaxLds)
+            return fail(BL_ERR_SHAPE, "%s: job %d: need N >= 0, 0 < K <= 16384, K %% 64 == 0 "
+                        "and tile(M) * K * (1 + element size) <= %zu (M=%lld N=%lld K=%lld)",
+                        name, j, bl::kFusedMaxLds, (long long)M, (long long)b.N, (long long)b.K);
+        if (b.reserved != 0)
+            return fail(BL_ERR_SHAPE, "%s: job %d: reserved must be 0", name, j);
+        if (!b.X || (b.N > 0 && (!b.Wp || !b.gamma || !b.Y)))
+            return fail(BL_ERR_NULL, "%s: job %d: NULL pointer", name, j);
+        if (!aligned(b.X, 16) || (b.Wp && !aligned(b.Wp, 16)) || (b.Xq && !aligned(b.Xq, 16)) ||
+            (b.gamma && !aligned(b.gamma, 4)) || (b.Y && !aligned(b.Y, 4)) ||
+            (b.d && !aligned(b.d, 4)))
+            return fail(BL_ERR_ALIGN, "%s: job %d: X, Wp, Xq need 16-byte alignment, "
+                        "gamma, Y, d 4-byte", name, j);
+        gj[j] = bl::GemvJob{b.X, b.Wp, b.gamma, b.Y, b.Xq, b.d, (int)b.N, (int)b.K,
+                            b.dtype == BL_BF16 ? 1 : 0};
+    }
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+    return launched(bl::launch_gemv_fused(gj, count, (int)M, static_cast<hipStream_t>(stream)),
+                    name);
+}
+
 BL_EXPORT bl_status bitlinear_ffn_relu2(const int8_t *Xq, const float *d, int64_t M, int64_t K,
                                         int64_t F, const uint8_t *Wg, const float *gamma_g,
                                         const uint8_t *Wu, const float *gamma_u,

@@ -71,4 +71,24 @@ __device__ __forceinline__ float rescale(int32_t acc, float c) {
     return __fmul_rn((float)acc, c);
 }
 
+// Per-token absmax int8 (iaiol.com article, 权重映射为三元值; model card,
+// 模型详情): with a = max |x| over the token,
+//   s = fl(127 / a),  q = clamp(rne(fl(x * s)), -127, 127),  d = fl(a / 127),
+// and a == 0 gives s = 0, q = 0, d = 0.  Every kernel that quantises
+// activations uses these three functions, so all paths give the same codes.
+__device__ __forceinline__ float act_inv_scale(float a) {
+    return a > 0.0f ? __fdiv_rn(127.0f, a) : 0.0f;
+}
+__device__ __forceinline__ float act_scale(float a) {
+    return a > 0.0f ? __fdiv_rn(a, 127.0f) : 0.0f;
+}
+__device__ __forceinline__ int act_code(float x, float s) {
+    float r = __builtin_rintf(__fmul_rn(x, s));
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
 }  // namespace bl

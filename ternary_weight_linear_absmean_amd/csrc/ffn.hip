@@ -32,11 +32,6 @@ __device__ __forceinline__ HZ h_and_z(float g, float u, bool gated, float gain) 
     return HZ{h, __fmul_rn(h, gain)};
 }
 
-__device__ __forceinline__ int quant1(float z, float s) {
-    float q = __builtin_rintf(__fmul_rn(z, s));
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (int)q;
-}
 
 __global__ __launch_bounds__(kThreads) void ffn_tail_kernel(
     const float *__restrict__ G, const float *__restrict__ U, const float *__restrict__ norm_w,
@@ -81,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void ffn_tail_kernel(
         ss += red_s[w];
     }
     const bool zero = !(a > 0.0f);
-    const float s = zero ? 0.0f : __fdiv_rn(127.0f, a);
+    const float s = act_inv_scale(a);
     int8_t *q_row = Hq + m * F;
     for (int f = 4 * threadIdx.x; f < F; f += 4 * kThreads) {
         const float4 gv = *reinterpret_cast<const float4 *>(g_row + f);
@@ -89,14 +84,14 @@ __global__ __launch_bounds__(kThreads) void ffn_tail_kernel(
                                 : make_float4(1.f, 1.f, 1.f, 1.f);
         const float4 wv = norm_w ? *reinterpret_cast<const float4 *>(norm_w + f)
                                  : make_float4(1.f, 1.f, 1.f, 1.f);
-        const uint32_t q = (uint32_t)(quant1(h_and_z(gv.x, uv.x, gated, wv.x).z, s) & 0xFF) |
-                           ((uint32_t)(quant1(h_and_z(gv.y, uv.y, gated, wv.y).z, s) & 0xFF) << 8) |
-                           ((uint32_t)(quant1(h_and_z(gv.z, uv.z, gated, wv.z).z, s) & 0xFF) << 16) |
-                           ((uint32_t)(quant1(h_and_z(gv.w, uv.w, gated, wv.w).z, s) & 0xFF) << 24);
+        const uint32_t q = (uint32_t)(act_code(h_and_z(gv.x, uv.x, gated, wv.x).z, s) & 0xFF) |
+                           ((uint32_t)(act_code(h_and_z(gv.y, uv.y, gated, wv.y).z, s) & 0xFF) << 8) |
+                           ((uint32_t)(act_code(h_and_z(gv.z, uv.z, gated, wv.z).z, s) & 0xFF) << 16) |
+                           ((uint32_t)(act_code(h_and_z(gv.w, uv.w, gated, wv.w).z, s) & 0xFF) << 24);
         *reinterpret_cast<uint32_t *>(q_row + f) = q;
     }
     if (threadIdx.x == 0) {
-        const float dhm = zero ? 0.0f : __fdiv_rn(a, 127.0f);
+        const float dhm = act_scale(a);
         dh[m] = dhm;
         // a row whose H * g is all zero has zero codes and scale 0
         dz[m] = zero ? 0.0f : (float)((double)dhm / sqrt(ss / (double)F + (double)eps));

@@ -25,6 +25,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnitsInFlight = 4;           // 16-byte loads issued before use
 constexpr int kXBytes = 64 * 1024;          // LDS budget for staged activations
+constexpr int kMaxJobs = kGemvMaxJobs;
 
 template <int L, int MT>
 __device__ __forceinline__ void dot_unit(const uint4 &w, const uint4 *xs, int gpc, int ul,
@@ -159,6 +160,240 @@ hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode kernel: per-token absmax int8 quantisation folded into the
+// GEMV, for several independent BitLinears in one launch.  Workgroups are
+// dealt to jobs in order (job j owns workgroups [wg_begin_j, wg_begin_j+1)).
+// Each workgroup
+//   1. issues its first packed-weight loads (they need no activations),
+//   2. reads the job's activation rows (L2-resident after the first
+//      workgroup), forms max |x| per token with a block reduction, and
+//      writes the int8 codes straight into LDS in transposed 16-byte groups
+//      (the first workgroup of the job also stores Xq and d to memory),
+//   3. runs the same unit loop and lane reduction as gemv_kernel, with the
+//      lane split L chosen per job.
+struct FusedJob {
+    const void *X;
+    const uint8_t *Wp;
+    const float *gamma;
+    float *Y;
+    int8_t *Xq;
+    float *d;
+    int N, K, dtype, lshift;          // lanes per row L = 1 << lshift
+    int wg_begin, pad;
+};
+
+struct FusedArgs {
+    FusedJob job[kMaxJobs];
+    int count, M;
+};
+
+#ifndef BL_FUSED_THREADS
+#define BL_FUSED_THREADS 256
+#endif
+constexpr int kFThreads = BL_FUSED_THREADS;
+constexpr int kXPre = 2;            // activation groups per thread loaded ahead of the weights
+
+// 16 consecutive activations as fp32 from their raw 16-byte words: four
+// words of fp32, or two words of bf16 (widening is exact).
+__device__ __forceinline__ void unpack_x16(const uint4 (&raw)[4], int dtype, float (&x)[16]) {
+    if (dtype == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[4 * t] = __uint_as_float(raw[t].x);
+            x[4 * t + 1] = __uint_as_float(raw[t].y);
+            x[4 * t + 2] = __uint_as_float(raw[t].z);
+            x[4 * t + 3] = __uint_as_float(raw[t].w);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t w4[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[8 * t + 2 * i] = bf16_lo(w4[i]);
+                x[8 * t + 2 * i + 1] = bf16_hi(w4[i]);
+            }
+        }
+    }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs args) {
+    extern __shared__ uint4 xs[];   // [MT][K / 16] transposed code groups, then [MT][K] fp32
+    __shared__ float red[kFThreads / 64][MT];
+    int j = 0;
+    for (int t = 1; t < args.count; ++t)
+        if ((int)blockIdx.x >= args.job[t].wg_begin) j = t;
+    const FusedJob &jb = args.job[j];
+    const int K = jb.K, N = jb.N, dtype = jb.dtype, lshift = jb.lshift;
+    const int L = 1 << lshift;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int r = lane >> lshift;
+    const int s = lane & (L - 1);
+    const int wg = (int)blockIdx.x - jb.wg_begin;
+    const int row = (wg * (kFThreads / 64) + (tid >> 6)) * (64 >> lshift) + r;
+    const int m0 = blockIdx.y * MT;
+    const int mt = min(MT, args.M - m0);
+    const int U = K / 64;
+    const int gpc = K / 16;
+    const uint4 *wrow = reinterpret_cast<const uint4 *>(jb.Wp + (size_t)max(min(row, N - 1), 0) * (K / 4));
+
+    // 1. Issue order matters: vector-memory loads retire in order, so the
+    //    first activation groups of this thread are requested before the
+    //    packed-weight loads; waiting for the activations then leaves the
+    //    weights in flight while the quantisation runs.
+    const int gsz = dtype == 0 ? 4 : 2;                       // uint4 per 16 elements
+    uint4 *xraw = xs + MT * gpc;                               // [MT][K / 16][gsz]
+    const char *xbase = reinterpret_cast<const char *>(jb.X);
+    const int ng = mt * gpc;                                   // (token, group) pairs
+    uint4 xr[kXPre][4];
+    // Both load sets are unconditional (clamped to valid addresses) so the
+    // wait for the activations can leave exactly the weight loads pending.
+#pragma unroll
+    for (int p = 0; p < kXPre; ++p) {
+        const int e = min(tid + p * kFThreads, ng - 1);
+        const int m = e / gpc, g = e - m * gpc;
+        // token row m0 + m starts K * (element size) = K * gsz bytes apart
+        const uint4 *src = reinterpret_cast<const uint4 *>(xbase + (size_t)(m0 + m) * K * gsz) +
+                           (size_t)g * gsz;
+        if (dtype == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xr[p][t] = src[t];
+        } else {
+            xr[p][0] = src[0];
+            xr[p][1] = src[1];
+        }
+    }
+    uint4 w[kUnitsInFlight];
+#pragma unroll
+    for (int q = 0; q < kUnitsInFlight; ++q)
+        w[q] = wrow[min(s + q * L, U - 1)];      // a job with N == 0 reads its own X here
+
+    // 2. activation quantisation into LDS: keep each group's raw words in LDS
+    //    and form max |x| per token; then quantise from LDS.
+    float amax[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) amax[m] = 0.0f;
+    // stage one group: raw words to LDS, fold max |x| into its token's amax
+    auto stage = [&](const uint4 (&raw)[4], int e) {
+        const int m = e / gpc, g = e - m * gpc;
+        float x[16];
+        unpack_x16(raw, dtype, x);
+        uint4 *dst = xraw + ((size_t)m * gpc + g) * gsz;
+        dst[0] = raw[0];
+        dst[1] = raw[1];
+        if (dtype == 0) { dst[2] = raw[2]; dst[3] = raw[3]; }
+        float a = 0.0f;
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) a = fmaxf(a, fabsf(x[i2]));
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+            if (mm == m) amax[mm] = fmaxf(amax[mm], a);
+    };
+#pragma unroll
+    for (int p = 0; p < kXPre; ++p) {
+        const int e = tid + p * kFThreads;
+        if (e < ng) stage(xr[p], e);
+    }
+    for (int e = tid + kXPre * kFThreads; e < ng; e += kFThreads) {
+        const int m = e / gpc, g = e - m * gpc;
+        const uint4 *src = reinterpret_cast<const uint4 *>(xbase + (size_t)(m0 + m) * K * gsz) +
+                           (size_t)g * gsz;
+        uint4 raw[4];
+        raw[0] = src[0];
+        raw[1] = src[1];
+        if (dtype == 0) { raw[2] = src[2]; raw[3] = src[3]; }
+        stage(raw, e);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            amax[m] = fmaxf(amax[m], __shfl_xor(amax[m], off));
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) red[tid >> 6][m] = amax[m];
+    }
+    __syncthreads();
+    const bool writer = (wg == 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float a = red[0][m];
+#pragma unroll
+        for (int v = 1; v < kFThreads / 64; ++v) a = fmaxf(a, red[v][m]);
+        if (m < mt) {
+            const float sc = act_inv_scale(a);
+            for (int g = tid; g < gpc; g += kFThreads) {
+                uint4 raw[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (t < gsz) raw[t] = xraw[((size_t)m * gpc + g) * gsz + t];
+                float x[16];
+                unpack_x16(raw, dtype, x);
+                uint32_t q4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    q4[t] = (uint32_t)(act_code(x[4 * t], sc) & 0xFF) |
+                            ((uint32_t)(act_code(x[4 * t + 1], sc) & 0xFF) << 8) |
+                            ((uint32_t)(act_code(x[4 * t + 2], sc) & 0xFF) << 16) |
+                            ((uint32_t)(act_code(x[4 * t + 3], sc) & 0xFF) << 24);
+                const uint4 qv = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+                if (writer && jb.Xq)
+                    *reinterpret_cast<uint4 *>(jb.Xq + (size_t)(m0 + m) * K + 16 * g) = qv;
+                xs[m * gpc + g] = transpose16(qv);
+            }
+            if (writer && jb.d && tid == 0)
+                jb.d[m0 + m] = act_scale(a);
+        }
+    }
+    __syncthreads();
+
+    // 3. dot products over this lane's units, software-pipelined
+    int acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0;
+    if (row < N) {
+        for (int u = s; u < U; u += L * kUnitsInFlight) {
+            uint4 wn[kUnitsInFlight];
+            const int un = u + L * kUnitsInFlight;
+            if (un < U) {
+#pragma unroll
+                for (int q = 0; q < kUnitsInFlight; ++q) wn[q] = wrow[min(un + q * L, U - 1)];
+            }
+#pragma unroll
+            for (int q = 0; q < kUnitsInFlight; ++q)
+                if (u + q * L < U)
+                    dot_unit<16, MT>(w[q], xs, gpc, u + q * L, acc);
+            if (un < U) {
+#pragma unroll
+                for (int q = 0; q < kUnitsInFlight; ++q) w[q] = wn[q];
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        for (int off = L >> 1; off > 0; off >>= 1)
+            acc[m] += __shfl_xor(acc[m], off);
+    if (row < N && s == 0) {
+        const float g = jb.gamma[0];
+        float dm[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float a = red[0][m];
+#pragma unroll
+            for (int v = 1; v < kFThreads / 64; ++v) a = fmaxf(a, red[v][m]);
+            dm[m] = act_scale(a);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < mt)
+                jb.Y[(size_t)(m0 + m) * N + row] = rescale(acc[m], __fmul_rn(g, dm[m]));
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
@@ -170,6 +405,55 @@ hipError_t launch_gemv(const int8_t *Xq, const float *d, int M, const uint8_t *W
     if (M == 2) return launch_m<2>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
     if (M <= 4) return launch_m<4>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
     return launch_m<8>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+}
+
+}  // namespace bl
+
+namespace bl {
+namespace {
+template <int MT>
+hipError_t launch_fused_mt(const FusedArgs &a, int grid_x, int max_k, int max_es, hipStream_t s) {
+    const dim3 grid(grid_x, (a.M + MT - 1) / MT);
+    hipLaunchKernelGGL((gemv_fused_kernel<MT>), grid, dim3(kFThreads), fused_lds_bytes(MT, max_k, max_es),
+                       s, a);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t s) {
+    FusedArgs a = {};
+    a.count = count;
+    a.M = M;
+    int wg = 0, max_k = 0, max_es = 2;
+    for (int j = 0; j < count; ++j) {
+        FusedJob &f = a.job[j];
+        f.X = jobs[j].X; f.Wp = jobs[j].Wp; f.gamma = jobs[j].gamma; f.Y = jobs[j].Y;
+        f.Xq = jobs[j].Xq; f.d = jobs[j].d;
+        f.N = jobs[j].N; f.K = jobs[j].K; f.dtype = jobs[j].dtype;
+        const int U = f.K / 64;
+        f.lshift = U >= 96 ? 6 : U >= 48 ? 5 : 4;
+#ifdef BL_FUSED_LSHIFT
+        f.lshift = BL_FUSED_LSHIFT;                     // tuning builds only
+#endif
+        const int rows_per_wg = (kFThreads / 64) * (64 >> f.lshift);
+        f.wg_begin = wg;
+        // a job with N == 0 still gets one workgroup when it must write Xq / d
+        const int n_wg = f.N > 0 ? (f.N + rows_per_wg - 1) / rows_per_wg : ((f.Xq || f.d) ? 1 : 0);
+        // A job with no output rows only quantises; its weight-row pointer
+        // aims at its own activations (K / 4 <= 2 K valid bytes) so the
+        // kernel's unconditional first loads stay in bounds.
+        if (f.N == 0)
+            f.Wp = static_cast<const uint8_t *>(f.X);
+        wg += n_wg;
+        max_k = f.K > max_k ? f.K : max_k;
+        max_es = (f.dtype == 0 ? 4 : 2) > max_es ? (f.dtype == 0 ? 4 : 2) : max_es;
+    }
+    if (wg == 0)
+        return hipSuccess;
+    if (M == 1) return launch_fused_mt<1>(a, wg, max_k, max_es, s);
+    if (M == 2) return launch_fused_mt<2>(a, wg, max_k, max_es, s);
+    if (M <= 4) return launch_fused_mt<4>(a, wg, max_k, max_es, s);
+    return launch_fused_mt<8>(a, wg, max_k, max_es, s);
 }
 
 }  // namespace bl

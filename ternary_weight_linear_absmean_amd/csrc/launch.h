@@ -31,6 +31,31 @@ hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *W
 // Largest M the VALU kernel takes in one pass over the weights.
 constexpr int kGemvMaxTokens = 8;
 
+// One job of the fused decode kernel (validated by the caller).
+struct GemvJob {
+    const void *X;
+    const uint8_t *Wp;
+    const float *gamma;
+    float *Y;
+    int8_t *Xq;
+    float *d;
+    int N, K, dtype;
+};
+constexpr int kGemvMaxJobs = 8;
+
+// Tokens per fused-kernel tile for M tokens, and its LDS bytes: the int8
+// codes (tile x K) plus the raw activations (tile x K x element size).
+constexpr int fused_tile(int M) { return M == 1 ? 1 : M == 2 ? 2 : M <= 4 ? 4 : 8; }
+constexpr size_t fused_lds_bytes(int tile, int K, int esize) {
+    return (size_t)tile * K * (1 + esize);
+}
+constexpr size_t kFusedMaxLds = 128 * 1024;
+
+// Per-token int8 quantisation of each job's X fused into its GEMV; all jobs
+// in one launch.  M <= 8, count <= kGemvMaxJobs,
+// fused_lds_bytes(fused_tile(M), K, esize) <= kFusedMaxLds for every job.
+hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t s);
+
 // Picks the VALU kernel for M <= kGemvMaxTokens and MFMA otherwise.
 hipError_t launch_bitlinear(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                             const float *gamma, int N, int K, float *Y, int32_t *acc,

@@ -123,11 +123,6 @@ __device__ __forceinline__ float4 load_x4(const void *X, int64_t i) {  // i % 4 
     }
 }
 
-__device__ __forceinline__ int quant1(float x, float s) {
-    float r = __builtin_rintf(__fmul_rn(x, s));
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-}
 
 __device__ __forceinline__ float block_max(float v, float *red) {
 #pragma unroll
@@ -163,23 +158,22 @@ __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const void *__re
             a = fmaxf(a, fabsf(load_x<DT>(X, base + k)));
     }
     a = block_max(a, red);
-    const bool zero = !(a > 0.0f);
-    const float s = zero ? 0.0f : __fdiv_rn(127.0f, a);
+    const float s = act_inv_scale(a);
     if constexpr (VEC) {
         for (int64_t k = 4 * (int64_t)threadIdx.x; k < K; k += 4 * kActThreads) {
             const float4 v = load_x4<DT>(X, base + k);
-            const uint32_t q = (uint32_t)(quant1(v.x, s) & 0xFF) |
-                               ((uint32_t)(quant1(v.y, s) & 0xFF) << 8) |
-                               ((uint32_t)(quant1(v.z, s) & 0xFF) << 16) |
-                               ((uint32_t)(quant1(v.w, s) & 0xFF) << 24);
+            const uint32_t q = (uint32_t)(act_code(v.x, s) & 0xFF) |
+                               ((uint32_t)(act_code(v.y, s) & 0xFF) << 8) |
+                               ((uint32_t)(act_code(v.z, s) & 0xFF) << 16) |
+                               ((uint32_t)(act_code(v.w, s) & 0xFF) << 24);
             *reinterpret_cast<uint32_t *>(Xq + base + k) = q;
         }
     } else {
         for (int64_t k = threadIdx.x; k < K; k += kActThreads)
-            Xq[base + k] = (int8_t)quant1(load_x<DT>(X, base + k), s);
+            Xq[base + k] = (int8_t)act_code(load_x<DT>(X, base + k), s);
     }
     if (threadIdx.x == 0)
-        d[m] = zero ? 0.0f : __fdiv_rn(a, 127.0f);
+        d[m] = act_scale(a);
 }
 
 }  // namespace

@@ -137,3 +137,38 @@ def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         bl.quant_act_absmax_i8(torch.zeros(2, 64))
+
+
+def test_fused_validation(lib):
+    J = _native.GemvJob
+
+    def job(**kw):
+        a = dict(X=0x10000, Wp=0x20000, gamma=0x30000, Y=0x40000, Xq=None, d=None, N=8,
+                 K=128, dtype=1, reserved=0)
+        a.update(kw)
+        return J(a["X"], a["Wp"], a["gamma"], a["Y"], a["Xq"], a["d"], a["N"], a["K"],
+                 a["dtype"], a["reserved"])
+
+    def call(jobs, M=1):
+        arr = (J * max(1, len(jobs)))(*jobs)
+        return lib.bitlinear_gemv_fused(arr, len(jobs), M, None)
+
+    assert lib.bitlinear_gemv_fused(None, 1, 1, None) == NULL
+    assert call([]) == SHAPE
+    assert call([job()] * 9) == SHAPE
+    assert call([job()], M=0) == SHAPE
+    assert call([job()], M=9) == SHAPE
+    assert call([job(K=96)]) == SHAPE
+    assert call([job(K=0)]) == SHAPE
+    assert call([job(K=16384)], M=8) == SHAPE          # LDS: 8 * 16384 * 3 > 128 KB
+    assert call([job(K=6912)], M=8) == SHAPE           # 8 * 6912 * 3 > 128 KB
+    assert call([job(K=6912, dtype=0)], M=4) == SHAPE  # 4 * 6912 * 5 > 128 KB
+    assert call([job(N=-1)]) == SHAPE
+    assert call([job(reserved=1)]) == SHAPE
+    assert call([job(dtype=5)]) == DTYPE
+    assert call([job(X=None)]) == NULL
+    assert call([job(Y=None)]) == NULL
+    assert call([job(X=0x10004)]) == ALIGN
+    assert call([job(Xq=0x50004)]) == ALIGN
+    assert call([job(d=0x50002)]) == ALIGN
+    assert call([job(), job(K=100)]) == SHAPE          # second job checked too

@@ -287,3 +287,84 @@ def test_ffn_zero_token(gpu):
     torch.cuda.synchronize()
     assert dh[1].item() == 0 and not Hq[1].any() and not Y[1].any()
     assert math.isfinite(Y.abs().max().item())
+
+
+# --------------------------------------------------------------- fused decode
+def _fused_case(gpu, M, shapes, dtype, seed, share_x=False, want_q=True):
+    jobs, refs = [], []
+    Xshared = None
+    for i, (K, N) in enumerate(shapes):
+        W, X = workloads.bitlinear_problem(seed + i, M, K, N, dtype=dtype)
+        if share_x:
+            Xshared = X if Xshared is None else Xshared
+            X = Xshared
+        Wp, g = _gpu_weight(gpu, W)
+        job = dict(X=X.cuda(), Wp=Wp, gamma=g)
+        if want_q:
+            job["Xq"] = None
+            job["d"] = None
+        jobs.append(job)
+        refs.append((X, W))
+    out = gpu.bitlinear_gemv_fused(jobs)
+    torch.cuda.synchronize()
+    for (X, W), j in zip(refs, out):
+        K = X.shape[1]
+        Xq_ref, d_ref = _ref_act(X)
+        Wp_ref, g_ref = oracle.quantize_weight(W.numpy())
+        acc_ref, Y_ref = oracle.bitlinear(Xq_ref, d_ref, Wp_ref, g_ref, K)
+        if want_q:
+            assert np.array_equal(j["Xq"].cpu().numpy(), Xq_ref)
+            assert np.array_equal(_f32_bits(j["d"].cpu().numpy()), _f32_bits(d_ref))
+        _assert_close(j["Y"].cpu().numpy(), Y_ref)
+        # bit-identical to the two-call path
+        Xq2, d2 = gpu.quant_act_absmax_i8(j["X"])
+        Y2 = gpu.bitlinear_gemv(Xq2, d2, j["Wp"], j["gamma"])
+        torch.cuda.synchronize()
+        assert torch.equal(j["Y"].view(torch.int32), Y2.view(torch.int32))
+
+
+def test_fused_decode_step(gpu):
+    shapes = [(s.K, s.N) for s in workloads.DECODE_SHAPES]
+    _fused_case(gpu, 1, shapes, torch.bfloat16, 500)
+
+
+def _fused_fits(M, K, dtype):
+    tile = 1 if M == 1 else 2 if M == 2 else 4 if M <= 4 else 8
+    es = 4 if dtype == torch.float32 else 2
+    return tile * K * (1 + es) <= 128 * 1024
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_fused_tokens_and_dtypes(gpu, M, dtype):
+    big = 6912 if _fused_fits(M, 6912, dtype) else 1024
+    _fused_case(gpu, M, [(2560, 640), (big, 97), (128, 1)], dtype, 600 + M)
+
+
+@pytest.mark.parametrize("M,K,dtype", [(1, 16384, torch.float32), (4, 6912, torch.bfloat16),
+                                       (8, 2560, torch.bfloat16)])
+def test_fused_large_lds(gpu, M, K, dtype):
+    """Staged activations above 64 KB of LDS (80, 83 and 61 KB)."""
+    assert _fused_fits(M, K, dtype)
+    _fused_case(gpu, M, [(K, 300)], dtype, 650 + M)
+
+
+def test_fused_shared_input_qkv(gpu):
+    _fused_case(gpu, 1, [(2560, 2560), (2560, 640), (2560, 640)], torch.bfloat16, 700,
+                share_x=True)
+
+
+def test_fused_eight_jobs_no_q_outputs(gpu):
+    shapes = [(64 * (i + 1), 33 * (i + 1)) for i in range(8)]
+    _fused_case(gpu, 2, shapes, torch.bfloat16, 800, want_q=False)
+
+
+def test_fused_zero_rows_job_still_quantises(gpu):
+    X = workloads.activations(workloads.generator(900), 1, 320)
+    Wp = torch.zeros(0, 80, dtype=torch.uint8, device="cuda")
+    g = torch.ones(1, device="cuda")
+    out = gpu.bitlinear_gemv_fused([dict(X=X.cuda(), Wp=Wp, gamma=g, Xq=None, d=None)])
+    torch.cuda.synchronize()
+    Xq_ref, d_ref = _ref_act(X)
+    assert np.array_equal(out[0]["Xq"].cpu().numpy(), Xq_ref)
+    assert out[0]["Y"].shape == (1, 0)
