@@ -15,8 +15,10 @@ is reported as ``decode_unfused``.
 
 Also measured in the same run and reported beside it: the prefill GEMM
 (M = 2048, K2560->N6912, int8 TOPS against the int8 MFMA peak), the prefill
-FFN tail (gate/up, ReLU² + subln + requant, down) and the CPU oracle on a
-bounded sample of the decode step.
+FFN tail (gate/up, ReLU² + subln + requant, down), one decode token through
+the full 30-layer linear stack (bitlinear_decode_stack: 521 MB of packed
+weights per token, tokens/s and GB/s) and the CPU oracle on a bounded sample
+of the decode step.
 
 Prints one JSON line.
 """
@@ -49,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--part", default="all", choices=["all", "decode", "gemm", "ffn"],
+    ap.add_argument("--part", default="all", choices=["all", "decode", "gemm", "ffn", "stack"],
                     help="restrict the GPU legs (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
@@ -213,6 +215,74 @@ def bench_ffn(bl, torch, workloads, steps, warmup):
     return dict(M=M, K=K, F=F, N=N, us=round(us, 2), TOPS=round(ops / us / 1e6, 1))
 
 
+STACK_SEED = 4242
+
+
+def stack_bytes(H, KV, F, layers):
+    """Algorithmic HBM bytes of one token through the stack: the packed
+    weights (the dominant term) plus the 7 gammas and the subln gain of each
+    layer; activations stay in L2-sized fp32 vectors and are not counted."""
+    per_layer = (2 * H * H + 2 * KV * H + 3 * F * H) // 4 + 7 * 4 + 4 * F
+    return layers * per_layer
+
+
+def bench_stack(bl, torch, workloads, steps, warmup):
+    """One decode token through the 30-layer 2B-class linear stack
+    (bitlinear_decode_stack), replayed from a HIP graph.  Each replay first
+    resets the residual stream to the same input token (a 10 KB copy standing
+    in for the embedding lookup), so every token does identical work; the
+    521 MB of packed weights exceed the Infinity Cache, so every token streams
+    them from HBM."""
+    H, KV, F, D, L = workloads.HIDDEN, workloads.KV, workloads.FFN, workloads.HEAD_DIM, \
+        workloads.LAYERS
+    layers = []
+    for l in range(L):
+        W = workloads.stack_layer_weights(STACK_SEED, l, H, KV, F, device="cuda")
+        Ld = {}
+        for name, gname in zip(bl.LAYER_WEIGHTS, bl.LAYER_GAMMAS):
+            Ld[name], Ld[gname] = bl.quant_weight_absmean_pack(W[name])
+        Ld["ffn_norm"] = torch.ones(F, dtype=torch.float32, device="cuda")
+        layers.append(Ld)
+        del W
+    torch.cuda.synchronize()
+    x0 = workloads.stack_token(STACK_SEED, H).cuda()
+    x = x0.clone()
+    ws = torch.empty((bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, H, KV, F),),
+                     dtype=torch.uint8, device="cuda")
+
+    def token(stream):
+        x.copy_(x0)
+        bl.bitlinear_decode_stack(layers, x, H, KV, F, D, ws=ws, stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        token(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            token(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(x).all())
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * t0.elapsed_time(t1) / steps
+    nbytes = stack_bytes(H, KV, F, L)
+    return dict(layers=L, H=H, KV=KV, F=F, head_dim=D, tokens=steps,
+                us_per_token=round(us, 2), tokens_per_s=round(1e6 / us, 1),
+                bytes_per_token=nbytes, GBs=round(nbytes / us / 1e3, 1),
+                frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                launches_per_token=1 + 8 * L)
+
+
 def cpu_baseline(torch, workloads, seconds):
     """The oracle, as it stands, on the decode step's four shapes, repeated
     for about `seconds` of wall time."""
@@ -276,6 +346,8 @@ def main():
         out["gemm"] = bench_gemm(bl, torch, workloads, max(10, args.steps // 8), 5)
     if args.part in ("all", "ffn"):
         out["ffn"] = bench_ffn(bl, torch, workloads, max(5, args.steps // 40), 2)
+    if args.part in ("all", "stack"):
+        out["stack"] = bench_stack(bl, torch, workloads, max(20, args.steps // 4), 5)
     if not args.no_cpu and args.part == "all":
         out["cpu_baseline"] = cpu_baseline(torch, workloads, args.cpu_seconds)
     print(json.dumps(out), flush=True)

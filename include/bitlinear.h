@@ -86,7 +86,8 @@ typedef enum {
 
 typedef enum {
     BL_OP_QUANT_WEIGHT = 0,   /* quant_weight_absmean_pack */
-    BL_OP_FFN_RELU2 = 1       /* bitlinear_ffn_relu2 */
+    BL_OP_FFN_RELU2 = 1,      /* bitlinear_ffn_relu2 */
+    BL_OP_DECODE_STACK = 2    /* bitlinear_decode_stack: N = H, K = KV, F = F */
 } bl_op;
 
 /* Largest K (and F) any call accepts: keeps |acc| <= 127 K exact in int32
@@ -231,6 +232,48 @@ bl_status bitlinear_ffn_relu2(const int8_t *Xq, const float *d,
                               const uint8_t *Wd, const float *gamma_d, int64_t N,
                               float *Y, int8_t *Hq, float *dh,
                               void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_decode_stack -- one decode token (M = 1) through a stack of
+ * BitNet b1.58 layers, every projection a W1.58A8 BitLinear.
+ * [CARD] 模型详情 (BitLinear without bias, W1.58A8, ReLU², subln);
+ * [NEWS] 权重映射为三元值 (ReLU² FFN, subln, per-token absmax activations).
+ *
+ * Per layer (the parts that are not BitLinears are one-token stand-ins):
+ *   q, k, v = BitLinear_q,k,v(x)        x: the fp32 residual stream [H]
+ *   a[h D + i] = v[(h / g) D + i]       attention over one key returns v;
+ *                                       g = (H / D) / (KV / D) query heads
+ *                                       share a key/value head
+ *   o = BitLinear_o(a);  x = x + o      (fp32 add)
+ *   y = bitlinear_ffn_relu2(x) (gated, subln gain ffn_norm, eps);  x = x + y
+ * Every BitLinear quantises its input per token as quant_act_absmax_i8.
+ *
+ *   layers   in   HOST array of n_layers bl_layer (device pointers inside):
+ *                 Wq [H][H/4], Wk, Wv [KV][H/4], Wo [H][H/4], Wg, Wu
+ *                 [F][H/4], Wd [H][F/4], their gammas, ffn_norm [F] or NULL.
+ *   dims          H, KV, F multiples of 64 (<= 16384), D divides H and KV,
+ *                 (KV / D) divides (H / D); eps >= 0.
+ *   x        in/out  fp32 [H], updated in place.
+ *   trace    out  NULL or fp32 [n_layers][5 H + 2 KV]: per layer x_in, q, k,
+ *                 v, o, x_mid (= x_in + o), y (the FFN output).
+ *   ws            >= bl_workspace_bytes(BL_OP_DECODE_STACK, 1, H, KV, F)
+ *                 bytes, 16-byte aligned.
+ */
+typedef struct {
+    const uint8_t *Wq, *Wk, *Wv, *Wo, *Wg, *Wu, *Wd;
+    const float *gq, *gk, *gv, *go, *gg, *gu, *gd;
+    const float *ffn_norm;
+} bl_layer;
+
+typedef struct {
+    int64_t H, KV, F, D;
+    float eps;
+    int32_t reserved;     /* must be 0 */
+} bl_stack_dims;
+
+bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers, const bl_stack_dims *dims,
+                                 float *x, float *trace, void *ws, size_t ws_bytes,
+                                 void *stream);
 
 /* Workspace bytes a call needs for the given sizes (0 for calls that need
  * none; arguments a call does not use are ignored). */

@@ -56,7 +56,7 @@ def _load():
     lib.ob_ffn_relu2.argtypes = [_p, _p, _i64, _i64, _i64,
                                  _p, _f32, _p, _f32, _p, _f32,
                                  _p, _f32, _i64,
-                                 _p, _p, _p, _p, _p, _p, _p, _p]
+                                 _p, _p, _p, _p, _p, _p, _p, _p, _p]
     _lib = lib
     return lib
 
@@ -174,7 +174,8 @@ def bitlinear(Xq, d, Wp, gamma, K):
 def ffn_relu2(Xq, d, Wg, gamma_g, Wu, gamma_u, norm_w, eps, Wd, gamma_d, K, F, N):
     """ReLU^2 FFN tail with subln RMSNorm and int8 requant; see oracle.c.
 
-    Returns dict(Y=float64 [M, N], Hq=int8 [M, F], dh=float32 [M], rms=float64 [M]).
+    Returns dict(Y=float64 [M, N], Hq=int8 [M, F], dh=float32 [M], rms=float64 [M],
+    Y32=float32 [M, N]: Y as the fp32 value that feeds a later quantisation).
     """
     Xq = _c(Xq, np.int8)
     d = _c(d, np.float32)
@@ -191,11 +192,56 @@ def ffn_relu2(Xq, d, Wg, gamma_g, Wu, gamma_u, norm_w, eps, Wd, gamma_d, K, F, N
     G = np.empty((M, F), dtype=np.float32)
     U = np.empty((M, F), dtype=np.float32)
     Zp = np.empty((M, F), dtype=np.float32)
+    Y32 = np.empty((M, N), dtype=np.float32)
     _load().ob_ffn_relu2(_ptr(Xq), _ptr(d), M, K, F,
                          _ptr(Wg), float(np.float32(gamma_g)),
                          _ptr(Wu), float(np.float32(gamma_u)),
                          _ptr(nw), float(eps),
                          _ptr(Wd), float(np.float32(gamma_d)), N,
                          _ptr(Y), _ptr(Hq), _ptr(dh), _ptr(rms),
-                         _ptr(scratch), _ptr(G), _ptr(U), _ptr(Zp))
-    return dict(Y=Y, Hq=Hq, dh=dh, rms=rms)
+                         _ptr(scratch), _ptr(G), _ptr(U), _ptr(Zp), _ptr(Y32))
+    return dict(Y=Y, Hq=Hq, dh=dh, rms=rms, Y32=Y32)
+
+
+def expand_heads(v, H, D):
+    """Attention over a single key returns v: query head h (of H / D) reads
+    key/value head h // g, g = (H / D) / (len(v) / D)."""
+    v = np.asarray(v, dtype=np.float32)
+    group = (H // D) // (v.shape[0] // D)
+    heads = v.reshape(-1, D)
+    return np.concatenate([heads[h // group] for h in range(H // D)]).astype(np.float32)
+
+
+def _bitlinear_f32(x, Wp, gamma, K):
+    """One M = 1 BitLinear on an fp32 activation row, output as fp32 (the
+    value a later quantisation sees)."""
+    Xq, d = quant_act(np.asarray(x, dtype=np.float32)[None, :])
+    return dequant_f32(ternary_acc(Xq, Wp, K), d, gamma)[0]
+
+
+def decode_stack(x0, layers, H, KV, F, D, eps):
+    """One decode token through the layers of a BitNet b1.58 stack (the
+    one-token stand-ins of attention as documented for bitlinear_decode_stack):
+        q, k, v = BitLinear(x); a = expand_heads(v); o = BitLinear(a);
+        x_mid = x + o; y = ffn_relu2(x_mid); x = x_mid + y.
+    Every value that feeds a later per-token quantisation (q, k, v, o, y and
+    the fp32 residual stream) is carried in fp32 with the rescale order of
+    dequant_f32, so the int8 decisions are those of the method in that
+    precision.  Returns (x_final, trace [n_layers, 5 H + 2 KV]) with the
+    per-layer x_in, q, k, v, o, x_mid, y."""
+    x = np.asarray(x0, dtype=np.float32).copy()
+    rows = []
+    for L in layers:
+        q = _bitlinear_f32(x, L["Wq"], L["gq"], H)
+        k = _bitlinear_f32(x, L["Wk"], L["gk"], H)
+        v = _bitlinear_f32(x, L["Wv"], L["gv"], H)
+        o = _bitlinear_f32(expand_heads(v, H, D), L["Wo"], L["go"], H)
+        x_mid = np.add(x, o, dtype=np.float32)
+        Xq, d = quant_act(x_mid[None, :])
+        f = ffn_relu2(Xq, d, L["Wg"], L["gg"], L["Wu"], L["gu"], L.get("ffn_norm"), eps,
+                      L["Wd"], L["gd"], H, F, H)
+        y = f["Y32"][0]
+        rows.append(np.concatenate([x, q, k, v, o, x_mid, y]))
+        x = np.add(x_mid, y, dtype=np.float32)
+    trace = np.stack(rows) if rows else np.zeros((0, 5 * H + 2 * KV), np.float32)
+    return x, trace

@@ -263,7 +263,8 @@ OB_EXPORT void ob_dequant_f32(const int32_t *acc, const float *d, float gamma,
  *     Hq, dh = ob_quant_act(Z')
  *     rms    = sqrt(sum_f H^2 / F + eps)        (fp64)
  *     Y      = acc_d * gamma_d * (dh / rms)     (fp64; 0 where dh == 0)
- * Outputs: Y [M][N] fp64, Hq [M][F] int8, dh [M] fp32, rms [M] fp64. */
+ * Outputs: Y [M][N] fp64, Hq [M][F] int8, dh [M] fp32, rms [M] fp64, and
+ * optionally Y32 [M][N], the fp32 value of Y (see below). */
 OB_EXPORT void ob_ffn_relu2(const int8_t *Xq, const float *d, int64_t M, int64_t K, int64_t F,
                             const uint8_t *Wg, float gamma_g,
                             const uint8_t *Wu, float gamma_u,
@@ -272,7 +273,7 @@ OB_EXPORT void ob_ffn_relu2(const int8_t *Xq, const float *d, int64_t M, int64_t
                             double *Y, int8_t *Hq, float *dh, double *rms,
                             int32_t *acc_scratch /* [M][max(F,N)] */,
                             float *G /* [M][F] */, float *U /* [M][F] */,
-                            float *Zp /* [M][F] */)
+                            float *Zp /* [M][F] */, float *Y32 /* [M][N] or NULL */)
 {
     ob_ternary_acc(Xq, Wg, M, F, K, acc_scratch);
     ob_dequant_f32(acc_scratch, d, gamma_g, M, F, G);
@@ -299,5 +300,14 @@ OB_EXPORT void ob_ffn_relu2(const int8_t *Xq, const float *d, int64_t M, int64_t
         double dz = dh[m] > 0.0f ? (double)dh[m] / rms[m] : 0.0;
         for (int64_t n = 0; n < N; ++n)
             Y[m * N + n] = (double)acc_scratch[m * N + n] * (double)gamma_d * dz;
+        if (Y32) {
+            /* The same output as an fp32 value, for when it feeds a later
+             * quantisation: dz rounded once to fp32, then the BitLinear rescale
+             * c = fl32(gamma_d * dz), Y = fl32(float(acc) * c). */
+            float dz32 = (float)dz;
+            float c = gamma_d * dz32;
+            for (int64_t n = 0; n < N; ++n)
+                Y32[m * N + n] = (float)acc_scratch[m * N + n] * c;
+        }
     }
 }

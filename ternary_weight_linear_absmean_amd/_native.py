@@ -26,7 +26,22 @@ STATUS = {0: "BL_OK", 1: "BL_ERR_NULL", 2: "BL_ERR_SHAPE", 3: "BL_ERR_DTYPE",
 
 EXPORTS = ["quant_weight_absmean_pack", "quant_act_absmax_i8", "bitlinear_gemv",
            "bitlinear_gemm", "bitlinear_gemv_fused", "bitlinear_ffn_relu2",
-           "bl_workspace_bytes", "bl_status_string", "bl_last_error", "bl_abi_version"]
+           "bitlinear_decode_stack", "bl_workspace_bytes", "bl_status_string",
+           "bl_last_error", "bl_abi_version"]
+BL_OP_DECODE_STACK = 2
+LAYER_WEIGHTS = ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd")
+LAYER_GAMMAS = ("gq", "gk", "gv", "go", "gg", "gu", "gd")
+
+
+class Layer(ctypes.Structure):
+    """bl_layer (include/bitlinear.h)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHTS + LAYER_GAMMAS + ("ffn_norm",)]
+
+
+class StackDims(ctypes.Structure):
+    """bl_stack_dims (include/bitlinear.h)."""
+    _fields_ = [("H", ctypes.c_int64), ("KV", ctypes.c_int64), ("F", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
 BL_MAX_JOBS = 8
 
 
@@ -69,6 +84,9 @@ def load():
         f.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _p]
     lib.bitlinear_gemv_fused.restype = st
     lib.bitlinear_gemv_fused.argtypes = [ctypes.POINTER(GemvJob), ctypes.c_int, _i64, _p]
+    lib.bitlinear_decode_stack.restype = st
+    lib.bitlinear_decode_stack.argtypes = [ctypes.POINTER(Layer), ctypes.c_int,
+                                           ctypes.POINTER(StackDims), _p, _p, _p, _sz, _p]
     lib.bitlinear_ffn_relu2.restype = st
     lib.bitlinear_ffn_relu2.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p,
                                         ctypes.c_float, _p, _p, _i64, _p, _p, _p, _p, _sz, _p]
@@ -263,3 +281,33 @@ def bitlinear_ffn_relu2(Xq, d, Wg, gamma_g, Wu, gamma_u, Wd, gamma_d, norm_w=Non
         _ptr(norm_w), float(eps), _ptr(Wd), _ptr(gamma_d), N, _ptr(Y), _ptr(Hq), _ptr(dh),
         _ptr(ws), ws.numel(), _stream(stream)))
     return (Y, Hq, dh) if want_debug else Y
+
+
+def bitlinear_decode_stack(layers, x, H, KV, F, D, eps=1e-5, trace=False, ws=None, stream=None):
+    """One decode token through len(layers) layers; x fp32 [H] is updated in
+    place.  Each layer is a dict with packed weights Wq..Wd (uint8), gammas
+    gq..gd (fp32 [1]) and optional ffn_norm (fp32 [F]).  With trace=True
+    returns the per-layer trace [n_layers, 5 H + 2 KV] (x_in, q, k, v, o,
+    x_mid, y)."""
+    _dev(x, torch.float32, "x")
+    n = len(layers)
+    arr = (Layer * max(1, n))()
+    for i, L in enumerate(layers):
+        vals = []
+        for k in LAYER_WEIGHTS:
+            vals.append(_dev(L[k], torch.uint8, k).data_ptr())
+        for k in LAYER_GAMMAS:
+            vals.append(_dev(L[k], torch.float32, k).data_ptr())
+        nw = L.get("ffn_norm")
+        vals.append(_dev(nw, torch.float32, "ffn_norm").data_ptr() if nw is not None else None)
+        arr[i] = Layer(*vals)
+    dims = StackDims(H, KV, F, D, float(eps), 0)
+    tr = None
+    if trace:
+        tr = torch.empty((n, 5 * H + 2 * KV), dtype=torch.float32, device=x.device)
+    need = workspace_bytes(BL_OP_DECODE_STACK, 1, H, KV, F)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
+    _check("bitlinear_decode_stack", load().bitlinear_decode_stack(
+        arr, n, ctypes.byref(dims), _ptr(x), _ptr(tr), _ptr(ws), ws.numel(), _stream(stream)))
+    return tr

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 
-SOURCES = ["api.cpp", "quant.hip", "gemv.hip", "gemm.hip", "ffn.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemv.hip", "gemm.hip", "ffn.hip", "stack.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

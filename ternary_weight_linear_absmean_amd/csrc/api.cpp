@@ -149,6 +149,9 @@ BL_EXPORT size_t bl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int
     switch (op) {
     case BL_OP_QUANT_WEIGHT: return round_up((size_t)N * sizeof(double), 256);
     case BL_OP_FFN_RELU2: return ffn_ws(M, F).total;
+    case BL_OP_DECODE_STACK:
+        if (N < 0 || K < 0 || F < 0 || N > 16384 || K > 16384 || F > 16384) return 0;
+        return round_up(bl::stack_ws_floats((int)N, (int)K, (int)F) * sizeof(float), 256);
     default: return 0;
     }
 }
@@ -327,4 +330,53 @@ BL_EXPORT bl_status bitlinear_ffn_relu2(const int8_t *Xq, const float *d, int64_
     if (e == hipSuccess && n > 0)
         e = bl::launch_bitlinear(hq, dz, m, Wd, gamma_d, n, f, Y, nullptr, s);
     return launched(e, name);
+}
+
+BL_EXPORT bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers,
+                                           const bl_stack_dims *dims, float *x, float *trace,
+                                           void *ws, size_t ws_bytes, void *stream) {
+    const char *name = "bitlinear_decode_stack";
+    if (!dims)
+        return fail(BL_ERR_NULL, "%s: dims is NULL", name);
+    const int64_t H = dims->H, KV = dims->KV, F = dims->F, D = dims->D;
+    if (n_layers < 0 || H <= 0 || KV <= 0 || F <= 0 || D <= 0 || H % 64 || KV % 64 ||
+        F % 64 || H > 16384 || KV > 16384 || F > 16384 || H % D || KV % D ||
+        (H / D) % (KV / D) || dims->reserved != 0 || !(dims->eps >= 0.0f))
+        return fail(BL_ERR_SHAPE, "%s: need n_layers >= 0; H, KV, F multiples of 64 up to "
+                    "16384; D dividing H and KV; KV/D dividing H/D; eps >= 0 (H=%lld KV=%lld "
+                    "F=%lld D=%lld)", name, (long long)H, (long long)KV, (long long)F,
+                    (long long)D);
+    if (n_layers == 0)
+        return ok();
+    if (!layers || !x)
+        return fail(BL_ERR_NULL, "%s: NULL layers or x", name);
+    if (!aligned(x, 16) || (trace && !aligned(trace, 16)))
+        return fail(BL_ERR_ALIGN, "%s: x and trace must be 16-byte aligned", name);
+    for (int l = 0; l < n_layers; ++l) {
+        const bl_layer &L = layers[l];
+        const uint8_t *w[7] = {L.Wq, L.Wk, L.Wv, L.Wo, L.Wg, L.Wu, L.Wd};
+        const float *g[7] = {L.gq, L.gk, L.gv, L.go, L.gg, L.gu, L.gd};
+        for (int i = 0; i < 7; ++i) {
+            if (!w[i] || !g[i])
+                return fail(BL_ERR_NULL, "%s: layer %d: NULL weight or gamma %d", name, l, i);
+            if (!aligned(w[i], 16) || !aligned(g[i], 4))
+                return fail(BL_ERR_ALIGN, "%s: layer %d: weights need 16-byte, gammas 4-byte "
+                            "alignment", name, l);
+        }
+        if (L.ffn_norm && !aligned(L.ffn_norm, 16))
+            return fail(BL_ERR_ALIGN, "%s: layer %d: ffn_norm must be 16-byte aligned", name, l);
+    }
+    const size_t need = bl_workspace_bytes(BL_OP_DECODE_STACK, 1, H, KV, F);
+    if (!ws || ws_bytes < need)
+        return fail(BL_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", name, ws_bytes,
+                    ws, need);
+    if (!aligned(ws, 16))
+        return fail(BL_ERR_ALIGN, "%s: ws must be 16-byte aligned", name);
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+    return launched(bl::launch_decode_stack(layers, n_layers, (int)H, (int)KV, (int)F, (int)D,
+                                            dims->eps, x, trace, static_cast<float *>(ws),
+                                            static_cast<hipStream_t>(stream)),
+                    name);
 }

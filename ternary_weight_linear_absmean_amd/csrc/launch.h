@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "bitlinear.h"
+
 namespace bl {
 
 // Offline weight path: fp64 row sums of |W| into `rowsum` [N], gamma, packing.
@@ -60,6 +62,19 @@ hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t 
 hipError_t launch_bitlinear(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                             const float *gamma, int N, int K, float *Y, int32_t *acc,
                             hipStream_t s);
+
+// One layer's weights for the decode stack (device pointers): the ABI's
+// bl_layer itself.
+using StackLayer = bl_layer;
+
+// Workspace (in floats) of launch_decode_stack.
+size_t stack_ws_floats(int H, int KV, int F);
+
+// One token (M = 1) through n_layers layers; x [H] fp32 is updated in place.
+// trace: NULL or [n_layers][5 H + 2 KV] = x_in, q, k, v, o, x_mid, y.
+hipError_t launch_decode_stack(const StackLayer *layers, int n_layers, int H, int KV, int F,
+                               int D, float eps, float *x, float *trace, float *ws,
+                               hipStream_t s);
 
 // FFN tail on fp32 G, U [M][F]: H = relu(G)^2 * U, Hq / dh = absmax int8 of
 // H * g, dz = dh / rms(H).  U == NULL: ungated; norm_w == NULL: unit gain.

@@ -172,3 +172,50 @@ def test_fused_validation(lib):
     assert call([job(Xq=0x50004)]) == ALIGN
     assert call([job(d=0x50002)]) == ALIGN
     assert call([job(), job(K=100)]) == SHAPE          # second job checked too
+
+
+def test_stack_validation(lib):
+    Lr = _native.Layer
+    D = _native.StackDims
+
+    def layer(**kw):
+        a = {k: 0x100000 + 0x1000 * i for i, k in enumerate(_native.LAYER_WEIGHTS)}
+        a.update({k: 0x200000 + 0x1000 * i for i, k in enumerate(_native.LAYER_GAMMAS)})
+        a["ffn_norm"] = None
+        a.update(kw)
+        return Lr(*[a[k] for k in _native.LAYER_WEIGHTS + _native.LAYER_GAMMAS + ("ffn_norm",)])
+
+    need = bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, 256, 128, 512)
+    assert need >= 4 * (2 * 256 + 2 * 128 + 2 * 512) + 512
+
+    def call(layers=None, n=None, H=256, KV=128, F=512, Dh=64, eps=1e-5, reserved=0,
+             x=A16, trace=None, ws=A16, wsb=1 << 20):
+        layers = [layer()] if layers is None else layers
+        arr = (Lr * max(1, len(layers)))(*layers)
+        dims = D(H, KV, F, Dh, eps, reserved)
+        return lib.bitlinear_decode_stack(arr, len(layers) if n is None else n,
+                                          ctypes.byref(dims), x, trace, ws, wsb, None)
+
+    assert lib.bitlinear_decode_stack(None, 1, None, A16, None, A16, 1 << 20, None) == NULL
+    assert call(n=-1) == SHAPE
+    assert call(H=200) == SHAPE
+    assert call(KV=96) == SHAPE
+    assert call(F=500) == SHAPE
+    assert call(H=32768, KV=128) == SHAPE
+    assert call(Dh=48) == SHAPE                       # D does not divide H
+    assert call(H=384, KV=256, Dh=128) == SHAPE       # 2 kv heads do not divide 3 query heads
+    assert call(eps=-1.0) == SHAPE
+    assert call(eps=float("nan")) == SHAPE
+    assert call(reserved=1) == SHAPE
+    assert call(n=0, x=None) == OK                    # no layers: nothing to do
+    assert call(x=None) == NULL
+    assert call(layers=[layer(), layer(Wd=None)]) == NULL
+    assert call(layers=[layer(gk=None)]) == NULL
+    assert call(x=A4) == ALIGN
+    assert call(trace=A4) == ALIGN
+    assert call(layers=[layer(Wv=0x100004)]) == ALIGN
+    assert call(layers=[layer(gq=0x200002)]) == ALIGN
+    assert call(layers=[layer(ffn_norm=0x300004)]) == ALIGN
+    assert call(wsb=need - 1) == WS
+    assert call(ws=None) == WS
+    assert call(ws=A4) == ALIGN

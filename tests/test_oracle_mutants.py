@@ -44,6 +44,7 @@ MUTANTS = [
     ("ffn_rms_multiplies", "(double)dh[m] / rms[m] : 0.0;", "(double)dh[m] * rms[m] : 0.0;"),
     ("ffn_rms_no_mean", "sqrt(ss / (double)F + (double)eps)", "sqrt(ss + (double)eps)"),
     ("ffn_gain_dropped", "float z = norm_w ? h * norm_w[f] : h;", "float z = h;"),
+    ("ffn_y32_scale_order", "float c = gamma_d * dz32;", "float c = gamma_d * (float)dh[m];"),
 ]
 
 
@@ -58,7 +59,8 @@ def _run_mutant(name, old, new, src_text, tmpdir):
                    capture_output=True)
     env = dict(os.environ, BITLINEAR_ORACLE_LIB=mut_so, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(HERE, "test_oracle_pins.py")],
+                        os.path.join(HERE, "test_oracle_pins.py"),
+                        os.path.join(HERE, "test_oracle_stack.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-400:]
 

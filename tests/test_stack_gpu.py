@@ -1,0 +1,132 @@
+"""GPU parity of bitlinear_decode_stack against the oracle's decode stack.
+
+The oracle runs the whole stack on its own weights and its own activations
+(oracle.decode_stack).  Each value that feeds a later per-token quantisation
+is carried in fp32 on both sides, so the first layer, which depends on x only
+through the same fp32 operations, must be bit-identical.  Later layers pass
+through the subln RMS (an fp64 sum whose order differs between the two
+sides); there the bar is 1e-3 relative to each trace segment's largest
+magnitude, and nearly every element is still expected to be bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-3
+NAMES = workloads.STACK_NAMES
+GAMMAS = ("gq", "gk", "gv", "go", "gg", "gu", "gd")
+
+
+def _build(bl, seed, n_layers, H, KV, F, gain=True):
+    """Quantise every weight on both sides; the packed bytes and gamma bits
+    must agree before the stack is compared."""
+    gpu_layers, ref_layers = [], []
+    for l in range(n_layers):
+        W = workloads.stack_layer_weights(seed, l, H, KV, F)
+        norm = workloads.stack_norm_gain(seed, l, F, gain) if gain is not None else None
+        G, R = {}, {}
+        for name, gname in zip(NAMES, GAMMAS):
+            Wp, g = bl.quant_weight_absmean_pack(W[name].cuda())
+            rp, rg = oracle.quantize_weight(W[name].numpy())
+            torch.cuda.synchronize()
+            assert np.array_equal(Wp.cpu().numpy(), rp), (l, name)
+            assert np.float32(g.item()).view(np.uint32) == np.float32(rg).view(np.uint32)
+            G[name], G[gname] = Wp, g
+            R[name], R[gname] = rp, rg
+        G["ffn_norm"] = norm.cuda() if norm is not None else None
+        R["ffn_norm"] = norm.numpy() if norm is not None else None
+        gpu_layers.append(G)
+        ref_layers.append(R)
+    return gpu_layers, ref_layers
+
+
+def _compare(trace, ref_trace, H, KV):
+    cuts = np.cumsum([0, H, H, KV, KV, H, H, H])
+    names = ("x_in", "q", "k", "v", "o", "x_mid", "y")
+    for l in range(ref_trace.shape[0]):
+        for i, name in enumerate(names):
+            got = trace[l, cuts[i]:cuts[i + 1]]
+            ref = ref_trace[l, cuts[i]:cuts[i + 1]]
+            if l == 0 and name != "y":
+                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (l, name)
+                continue
+            scale = np.abs(ref).max()
+            err = np.abs(got.astype(np.float64) - ref).max()
+            assert err <= RTOL * scale, (l, name, err, scale)
+    same = np.mean(trace.view(np.uint32) == ref_trace.view(np.uint32))
+    assert same >= 0.999, same
+
+
+@pytest.mark.parametrize("H,KV,F,D,n_layers,gain", [
+    (256, 128, 512, 64, 3, True),      # 4 query heads on 2 key/value heads
+    (192, 192, 320, 64, 2, True),      # one query head per key/value head; F % 128 = 64
+    (256, 64, 448, 32, 2, None),       # 8 query heads on 2; no subln gain
+    (2560, 640, 6912, 128, 2, True),   # 2B-class layer dimensions
+], ids=["grouped", "mha_ragged", "gqa8_nogain", "full_dims"])
+def test_decode_stack_matches_oracle(gpu, H, KV, F, D, n_layers, gain):
+    bl = gpu
+    seed = 11 + H + n_layers
+    gl, rl = _build(bl, seed, n_layers, H, KV, F, gain)
+    x0 = workloads.stack_token(seed, H)
+    x = x0.cuda()
+    trace = bl.bitlinear_decode_stack(gl, x, H, KV, F, D, eps=1e-5, trace=True)
+    torch.cuda.synchronize()
+    ref_x, ref_trace = oracle.decode_stack(x0.numpy(), rl, H, KV, F, D, 1e-5)
+    _compare(trace.cpu().numpy(), ref_trace, H, KV)
+    got = x.cpu().numpy()
+    err = np.abs(got.astype(np.float64) - ref_x).max()
+    assert err <= RTOL * np.abs(ref_x).max()
+
+
+def test_decode_stack_trace_off_and_no_layers(gpu):
+    bl = gpu
+    H, KV, F, D = 256, 128, 512, 64
+    gl, _ = _build(bl, 5, 2, H, KV, F)
+    x0 = workloads.stack_token(5, H).cuda()
+    x1 = x0.clone()
+    t = bl.bitlinear_decode_stack(gl, x1, H, KV, F, D, trace=True)
+    x2 = x0.clone()
+    assert bl.bitlinear_decode_stack(gl, x2, H, KV, F, D) is None
+    x3 = x0.clone()
+    bl.bitlinear_decode_stack([], x3, H, KV, F, D)
+    torch.cuda.synchronize()
+    assert torch.equal(x1, x2)                       # the trace does not change the result
+    assert torch.equal(x3, x0)                       # no layers: x untouched
+    assert torch.equal(t[0, :H], x0)
+    assert not torch.equal(x1, x0)
+
+
+def test_decode_stack_graph_replay(gpu):
+    # The stack records no memset and no host synchronisation, so it can be
+    # captured once and replayed; every replay must equal the eager result.
+    bl = gpu
+    H, KV, F, D = 256, 64, 512, 32
+    gl, _ = _build(bl, 9, 2, H, KV, F)
+    x0 = workloads.stack_token(9, H).cuda()
+    ref = x0.clone()
+    ws = torch.empty(bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, H, KV, F),
+                     dtype=torch.uint8, device="cuda")
+    bl.bitlinear_decode_stack(gl, ref, H, KV, F, D, ws=ws)
+    torch.cuda.synchronize()
+    x = x0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bl.bitlinear_decode_stack(gl, x, H, KV, F, D, ws=ws, stream=s)   # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bl.bitlinear_decode_stack(gl, x, H, KV, F, D, ws=ws,
+                                  stream=torch.cuda.current_stream())
+    for _ in range(3):
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x, ref)
+        _ = (x0 * 2).sum().item()                    # eager work between replays

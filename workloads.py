@@ -118,3 +118,35 @@ LAYER_PROJS: List[Tuple[str, int, int]] = [
 
 def stack_seed(layer: int, proj: int) -> int:
     return 7 * layer + proj
+
+
+STACK_NAMES = ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd")
+HEAD_DIM = 128
+
+
+def stack_layer_weights(seed: int, layer: int, H: int, KV: int, F: int, device="cpu"):
+    """fp32 master weights of one layer of the linear stack, in projection
+    order q, k, v, o, gate, up, down ([N, K] each), one generator per
+    projection seeded with seed + stack_seed(layer, p).  With device="cuda"
+    the generator and the draw are on the GPU (bench-sized stacks)."""
+    dims = [(H, H), (KV, H), (KV, H), (H, H), (F, H), (F, H), (H, F)]
+    out = {}
+    for p, (name, (N, K)) in enumerate(zip(STACK_NAMES, dims)):
+        g = torch.Generator(device=device)
+        g.manual_seed(int(seed + stack_seed(layer, p)))
+        out[name] = torch.randn(N, K, generator=g, dtype=torch.float32, device=device) * W_STD
+    return out
+
+
+def stack_norm_gain(seed: int, layer: int, F: int, gain: bool = True):
+    """subln gain [F] of one layer: ones (random init), or with gain=True
+    U(0.5, 1.5) so that the gain is exercised."""
+    if not gain:
+        return torch.ones(F, dtype=torch.float32)
+    g = generator(seed + 1_000_003 + layer)
+    return 0.5 + torch.rand(F, generator=g, dtype=torch.float32)
+
+
+def stack_token(seed: int, H: int) -> torch.Tensor:
+    """fp32 residual-stream input [H] for one decode token (outliers on)."""
+    return activations(generator(seed + 2_000_003), 1, H, dtype=torch.float32)[0]
