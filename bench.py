@@ -250,37 +250,44 @@ def bench_stack(bl, torch, workloads, steps, warmup):
     ws = torch.empty((bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, H, KV, F),),
                      dtype=torch.uint8, device="cuda")
 
-    def token(stream):
-        x.copy_(x0)
-        bl.bitlinear_decode_stack(layers, x, H, KV, F, D, ws=ws, stream=stream)
+    def timed(path, n):
+        def token(stream):
+            x.copy_(x0)
+            bl.bitlinear_decode_stack(layers, x, H, KV, F, D, ws=ws, stream=stream, path=path)
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        token(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
             token(side)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(x).all())
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    us = 1000.0 * t0.elapsed_time(t1) / steps
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                token(side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(x).all())
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * t0.elapsed_time(t1) / n
+
     nbytes = stack_bytes(H, KV, F, L)
+    us = timed(bl.BL_STACK_PERSISTENT, steps)
+    us_l = timed(bl.BL_STACK_LAUNCHES, max(10, steps // 4))
     return dict(layers=L, H=H, KV=KV, F=F, head_dim=D, tokens=steps,
+                path="persistent", launches_per_token=2 + (L - 1) // 16,
                 us_per_token=round(us, 2), tokens_per_s=round(1e6 / us, 1),
                 bytes_per_token=nbytes, GBs=round(nbytes / us / 1e3, 1),
                 frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                launches_per_token=1 + 8 * L)
+                launches_path=dict(us_per_token=round(us_l, 2),
+                                   GBs=round(nbytes / us_l / 1e3, 1),
+                                   launches_per_token=2 + 8 * L))
 
 
 def cpu_baseline(torch, workloads, seconds):

@@ -252,7 +252,7 @@ bl_status bitlinear_ffn_relu2(const int8_t *Xq, const float *d,
  *                 Wq [H][H/4], Wk, Wv [KV][H/4], Wo [H][H/4], Wg, Wu
  *                 [F][H/4], Wd [H][F/4], their gammas, ffn_norm [F] or NULL.
  *   dims          H, KV, F multiples of 64 (<= 16384), D divides H and KV,
- *                 (KV / D) divides (H / D); eps >= 0.
+ *                 (KV / D) divides (H / D); eps >= 0; path (below).
  *   x        in/out  fp32 [H], updated in place.
  *   trace    out  NULL or fp32 [n_layers][5 H + 2 KV]: per layer x_in, q, k,
  *                 v, o, x_mid (= x_in + o), y (the FFN output).
@@ -268,8 +268,23 @@ typedef struct {
 typedef struct {
     int64_t H, KV, F, D;
     float eps;
-    int32_t reserved;     /* must be 0 */
+    int32_t path;         /* BL_STACK_AUTO, BL_STACK_LAUNCHES or BL_STACK_PERSISTENT */
 } bl_stack_dims;
+
+/* How bitlinear_decode_stack runs (same results either way):
+ *   BL_STACK_LAUNCHES    one launch per step (fused q/k/v, head expansion,
+ *                        fused o, residual, fused gate/up, FFN tail, down,
+ *                        residual): 8 launches per layer.
+ *   BL_STACK_PERSISTENT  one launch per 16 layers with one workgroup per
+ *                        compute unit; the steps are separated by grid-wide
+ *                        barriers and each step's weights are fetched while
+ *                        the previous barrier resolves.  BL_ERR_SHAPE if the
+ *                        sizes exceed its per-workgroup limits on the device
+ *                        (2B-class sizes fit).  If the grid is not resident
+ *                        as a whole (the device shared with other work) a
+ *                        barrier gives up after 1 s and x is filled with NaN.
+ *   BL_STACK_AUTO        persistent where it fits, else launches. */
+enum { BL_STACK_AUTO = 0, BL_STACK_LAUNCHES = 1, BL_STACK_PERSISTENT = 2 };
 
 bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers, const bl_stack_dims *dims,
                                  float *x, float *trace, void *ws, size_t ws_bytes,

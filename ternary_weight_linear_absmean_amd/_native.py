@@ -41,7 +41,12 @@ class Layer(ctypes.Structure):
 class StackDims(ctypes.Structure):
     """bl_stack_dims (include/bitlinear.h)."""
     _fields_ = [("H", ctypes.c_int64), ("KV", ctypes.c_int64), ("F", ctypes.c_int64),
-                ("D", ctypes.c_int64), ("eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("D", ctypes.c_int64), ("eps", ctypes.c_float), ("path", ctypes.c_int32)]
+
+
+BL_STACK_AUTO = 0
+BL_STACK_LAUNCHES = 1
+BL_STACK_PERSISTENT = 2
 BL_MAX_JOBS = 8
 
 
@@ -283,12 +288,13 @@ def bitlinear_ffn_relu2(Xq, d, Wg, gamma_g, Wu, gamma_u, Wd, gamma_d, norm_w=Non
     return (Y, Hq, dh) if want_debug else Y
 
 
-def bitlinear_decode_stack(layers, x, H, KV, F, D, eps=1e-5, trace=False, ws=None, stream=None):
+def bitlinear_decode_stack(layers, x, H, KV, F, D, eps=1e-5, trace=False, ws=None, stream=None,
+                           path=BL_STACK_AUTO):
     """One decode token through len(layers) layers; x fp32 [H] is updated in
     place.  Each layer is a dict with packed weights Wq..Wd (uint8), gammas
     gq..gd (fp32 [1]) and optional ffn_norm (fp32 [F]).  With trace=True
     returns the per-layer trace [n_layers, 5 H + 2 KV] (x_in, q, k, v, o,
-    x_mid, y)."""
+    x_mid, y).  path: BL_STACK_AUTO, BL_STACK_LAUNCHES or BL_STACK_PERSISTENT."""
     _dev(x, torch.float32, "x")
     n = len(layers)
     arr = (Layer * max(1, n))()
@@ -301,7 +307,7 @@ def bitlinear_decode_stack(layers, x, H, KV, F, D, eps=1e-5, trace=False, ws=Non
         nw = L.get("ffn_norm")
         vals.append(_dev(nw, torch.float32, "ffn_norm").data_ptr() if nw is not None else None)
         arr[i] = Layer(*vals)
-    dims = StackDims(H, KV, F, D, float(eps), 0)
+    dims = StackDims(H, KV, F, D, float(eps), int(path))
     tr = None
     if trace:
         tr = torch.empty((n, 5 * H + 2 * KV), dtype=torch.float32, device=x.device)

@@ -341,9 +341,10 @@ BL_EXPORT bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers,
     const int64_t H = dims->H, KV = dims->KV, F = dims->F, D = dims->D;
     if (n_layers < 0 || H <= 0 || KV <= 0 || F <= 0 || D <= 0 || H % 64 || KV % 64 ||
         F % 64 || H > 16384 || KV > 16384 || F > 16384 || H % D || KV % D ||
-        (H / D) % (KV / D) || dims->reserved != 0 || !(dims->eps >= 0.0f))
+        (H / D) % (KV / D) || dims->path < BL_STACK_AUTO || dims->path > BL_STACK_PERSISTENT ||
+        !(dims->eps >= 0.0f))
         return fail(BL_ERR_SHAPE, "%s: need n_layers >= 0; H, KV, F multiples of 64 up to "
-                    "16384; D dividing H and KV; KV/D dividing H/D; eps >= 0 (H=%lld KV=%lld "
+                    "16384; D dividing H and KV; KV/D dividing H/D; eps >= 0; path 0..2 (H=%lld KV=%lld "
                     "F=%lld D=%lld)", name, (long long)H, (long long)KV, (long long)F,
                     (long long)D);
     if (n_layers == 0)
@@ -375,8 +376,12 @@ BL_EXPORT bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers,
     bl_status st = check_arch();
     if (st != BL_OK)
         return st;
+    if (dims->path == BL_STACK_PERSISTENT && !bl::stack_persistent_fits((int)H, (int)KV, (int)F, (int)D))
+        return fail(BL_ERR_SHAPE, "%s: H=%lld KV=%lld F=%lld exceed the persistent path's "
+                    "per-workgroup limits on this device", name, (long long)H, (long long)KV,
+                    (long long)F);
     return launched(bl::launch_decode_stack(layers, n_layers, (int)H, (int)KV, (int)F, (int)D,
                                             dims->eps, x, trace, static_cast<float *>(ws),
-                                            static_cast<hipStream_t>(stream)),
+                                            dims->path, static_cast<hipStream_t>(stream)),
                     name);
 }

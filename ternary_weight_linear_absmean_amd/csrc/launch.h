@@ -67,14 +67,34 @@ hipError_t launch_bitlinear(const int8_t *Xq, const float *d, int M, const uint8
 // bl_layer itself.
 using StackLayer = bl_layer;
 
-// Workspace (in floats) of launch_decode_stack.
+// Workspace of launch_decode_stack, carved from the caller's buffer: every
+// region starts on a 64-float boundary.  The per-step path uses q..Hq, the
+// persistent path q, k and the tagged region.
+struct StackWs {
+    float *q, *a, *o, *y, *k, *v, *G, *U, *dh, *dz;
+    int8_t *Hq;
+    float *tagged;
+};
 size_t stack_ws_floats(int H, int KV, int F);
+StackWs stack_ws(float *ws, int H, int KV, int F);
+
+// Decode-stack paths (bl_stack_dims.path).
+enum StackPath { kStackAuto = 0, kStackLaunches = 1, kStackPersistent = 2 };
 
 // One token (M = 1) through n_layers layers; x [H] fp32 is updated in place.
 // trace: NULL or [n_layers][5 H + 2 KV] = x_in, q, k, v, o, x_mid, y.
 hipError_t launch_decode_stack(const StackLayer *layers, int n_layers, int H, int KV, int F,
-                               int D, float eps, float *x, float *trace, float *ws,
+                               int D, float eps, float *x, float *trace, float *ws, int path,
                                hipStream_t s);
+
+// The persistent path: one launch per 16 layers, one workgroup per compute
+// unit of the current device.  fits() says whether these sizes fit its
+// per-workgroup limits on the current device.
+size_t stack_persistent_ws_floats(int H, int KV, int F);
+bool stack_persistent_fits(int H, int KV, int F, int D);
+hipError_t launch_decode_stack_persistent(const StackLayer *layers, int n_layers, int H, int KV,
+                                          int F, int D, float eps, float *x, float *trace,
+                                          const StackWs &ws, hipStream_t s);
 
 // FFN tail on fp32 G, U [M][F]: H = relu(G)^2 * U, Hq / dh = absmax int8 of
 // H * g, dz = dh / rms(H).  U == NULL: ungated; norm_w == NULL: unit gain.

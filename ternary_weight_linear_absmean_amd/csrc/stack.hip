@@ -46,28 +46,39 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(float *__restrict__ 
 
 }  // namespace
 
+namespace {
+size_t r64(size_t n) { return (n + 63) / 64 * 64; }
+}  // namespace
+
 size_t stack_ws_floats(int H, int KV, int F) {
-    // q, a, o, y: H each; k, v: KV each; G, U: F each; dh, dz: 1 each;
-    // Hq: F bytes = F / 4 floats.  Every region starts on a 64-float boundary.
-    auto r = [](size_t n) { return (n + 63) / 64 * 64; };
-    return 4 * r(H) + 2 * r(KV) + 2 * r(F) + 2 * r(1) + r(F / 4 + 1);
+    // q, a, o, y: H each; k, v: KV each; G, U: F each; dh, dz: 1 each; Hq: F
+    // bytes = F / 4 floats; then the persistent path's tagged vectors.
+    return 4 * r64(H) + 2 * r64(KV) + 2 * r64(F) + 2 * r64(1) + r64(F / 4 + 1) +
+           r64(stack_persistent_ws_floats(H, KV, F));
+}
+
+StackWs stack_ws(float *ws, int H, int KV, int F) {
+    StackWs w;
+    float *p = ws;
+    auto take = [&](size_t n) { float *r = p; p += r64(n); return r; };
+    w.q = take(H); w.a = take(H); w.o = take(H); w.y = take(H);
+    w.k = take(KV); w.v = take(KV);
+    w.G = take(F); w.U = take(F);
+    w.dh = take(1); w.dz = take(1);
+    w.Hq = reinterpret_cast<int8_t *>(take(F / 4 + 1));
+    w.tagged = take(stack_persistent_ws_floats(H, KV, F));
+    return w;
 }
 
 hipError_t launch_decode_stack(const StackLayer *layers, int n_layers, int H, int KV, int F,
-                               int D, float eps, float *x, float *trace, float *ws,
+                               int D, float eps, float *x, float *trace, float *ws, int path,
                                hipStream_t s) {
-    auto r = [](size_t n) { return (n + 63) / 64 * 64; };
-    float *q = ws;
-    float *a = q + r(H);
-    float *o = a + r(H);
-    float *y = o + r(H);
-    float *k = y + r(H);
-    float *v = k + r(KV);
-    float *G = v + r(KV);
-    float *U = G + r(F);
-    float *dh = U + r(F);
-    float *dz = dh + r(1);
-    int8_t *Hq = reinterpret_cast<int8_t *>(dz + r(1));
+    const StackWs w = stack_ws(ws, H, KV, F);
+    if (path == kStackPersistent || (path == kStackAuto && stack_persistent_fits(H, KV, F, D)))
+        return launch_decode_stack_persistent(layers, n_layers, H, KV, F, D, eps, x, trace, w, s);
+    float *q = w.q, *a = w.a, *o = w.o, *y = w.y, *k = w.k, *v = w.v, *G = w.G, *U = w.U;
+    float *dh = w.dh, *dz = w.dz;
+    int8_t *Hq = w.Hq;
     const int group = (H / D) / (KV / D);
     const size_t stride = (size_t)5 * H + 2 * KV;     // x_in q k v o x_mid y
     const dim3 eb((H + kThreads - 1) / kThreads);

@@ -188,11 +188,11 @@ def test_stack_validation(lib):
     need = bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, 256, 128, 512)
     assert need >= 4 * (2 * 256 + 2 * 128 + 2 * 512) + 512
 
-    def call(layers=None, n=None, H=256, KV=128, F=512, Dh=64, eps=1e-5, reserved=0,
+    def call(layers=None, n=None, H=256, KV=128, F=512, Dh=64, eps=1e-5, path=0,
              x=A16, trace=None, ws=A16, wsb=1 << 20):
         layers = [layer()] if layers is None else layers
         arr = (Lr * max(1, len(layers)))(*layers)
-        dims = D(H, KV, F, Dh, eps, reserved)
+        dims = D(H, KV, F, Dh, eps, path)
         return lib.bitlinear_decode_stack(arr, len(layers) if n is None else n,
                                           ctypes.byref(dims), x, trace, ws, wsb, None)
 
@@ -206,7 +206,8 @@ def test_stack_validation(lib):
     assert call(H=384, KV=256, Dh=128) == SHAPE       # 2 kv heads do not divide 3 query heads
     assert call(eps=-1.0) == SHAPE
     assert call(eps=float("nan")) == SHAPE
-    assert call(reserved=1) == SHAPE
+    assert call(path=3) == SHAPE
+    assert call(path=-1) == SHAPE
     assert call(n=0, x=None) == OK                    # no layers: nothing to do
     assert call(x=None) == NULL
     assert call(layers=[layer(), layer(Wd=None)]) == NULL

@@ -62,19 +62,23 @@ def _compare(trace, ref_trace, H, KV):
     assert same >= 0.999, same
 
 
+PATHS = pytest.mark.parametrize("path", [1, 2], ids=["launches", "persistent"])
+
+
+@PATHS
 @pytest.mark.parametrize("H,KV,F,D,n_layers,gain", [
     (256, 128, 512, 64, 3, True),      # 4 query heads on 2 key/value heads
     (192, 192, 320, 64, 2, True),      # one query head per key/value head; F % 128 = 64
     (256, 64, 448, 32, 2, None),       # 8 query heads on 2; no subln gain
     (2560, 640, 6912, 128, 2, True),   # 2B-class layer dimensions
 ], ids=["grouped", "mha_ragged", "gqa8_nogain", "full_dims"])
-def test_decode_stack_matches_oracle(gpu, H, KV, F, D, n_layers, gain):
+def test_decode_stack_matches_oracle(gpu, H, KV, F, D, n_layers, gain, path):
     bl = gpu
     seed = 11 + H + n_layers
     gl, rl = _build(bl, seed, n_layers, H, KV, F, gain)
     x0 = workloads.stack_token(seed, H)
     x = x0.cuda()
-    trace = bl.bitlinear_decode_stack(gl, x, H, KV, F, D, eps=1e-5, trace=True)
+    trace = bl.bitlinear_decode_stack(gl, x, H, KV, F, D, eps=1e-5, trace=True, path=path)
     torch.cuda.synchronize()
     ref_x, ref_trace = oracle.decode_stack(x0.numpy(), rl, H, KV, F, D, 1e-5)
     _compare(trace.cpu().numpy(), ref_trace, H, KV)
@@ -83,17 +87,18 @@ def test_decode_stack_matches_oracle(gpu, H, KV, F, D, n_layers, gain):
     assert err <= RTOL * np.abs(ref_x).max()
 
 
-def test_decode_stack_trace_off_and_no_layers(gpu):
+@PATHS
+def test_decode_stack_trace_off_and_no_layers(gpu, path):
     bl = gpu
     H, KV, F, D = 256, 128, 512, 64
     gl, _ = _build(bl, 5, 2, H, KV, F)
     x0 = workloads.stack_token(5, H).cuda()
     x1 = x0.clone()
-    t = bl.bitlinear_decode_stack(gl, x1, H, KV, F, D, trace=True)
+    t = bl.bitlinear_decode_stack(gl, x1, H, KV, F, D, trace=True, path=path)
     x2 = x0.clone()
-    assert bl.bitlinear_decode_stack(gl, x2, H, KV, F, D) is None
+    assert bl.bitlinear_decode_stack(gl, x2, H, KV, F, D, path=path) is None
     x3 = x0.clone()
-    bl.bitlinear_decode_stack([], x3, H, KV, F, D)
+    bl.bitlinear_decode_stack([], x3, H, KV, F, D, path=path)
     torch.cuda.synchronize()
     assert torch.equal(x1, x2)                       # the trace does not change the result
     assert torch.equal(x3, x0)                       # no layers: x untouched
@@ -101,7 +106,8 @@ def test_decode_stack_trace_off_and_no_layers(gpu):
     assert not torch.equal(x1, x0)
 
 
-def test_decode_stack_graph_replay(gpu):
+@PATHS
+def test_decode_stack_graph_replay(gpu, path):
     # The stack records no memset and no host synchronisation, so it can be
     # captured once and replayed; every replay must equal the eager result.
     bl = gpu
@@ -111,18 +117,18 @@ def test_decode_stack_graph_replay(gpu):
     ref = x0.clone()
     ws = torch.empty(bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, H, KV, F),
                      dtype=torch.uint8, device="cuda")
-    bl.bitlinear_decode_stack(gl, ref, H, KV, F, D, ws=ws)
+    bl.bitlinear_decode_stack(gl, ref, H, KV, F, D, ws=ws, path=path)
     torch.cuda.synchronize()
     x = x0.clone()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        bl.bitlinear_decode_stack(gl, x, H, KV, F, D, ws=ws, stream=s)   # warm-up
+        bl.bitlinear_decode_stack(gl, x, H, KV, F, D, ws=ws, stream=s, path=path)   # warm-up
     torch.cuda.current_stream().wait_stream(s)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         bl.bitlinear_decode_stack(gl, x, H, KV, F, D, ws=ws,
-                                  stream=torch.cuda.current_stream())
+                                  stream=torch.cuda.current_stream(), path=path)
     for _ in range(3):
         x.copy_(x0)
         torch.cuda.synchronize()
@@ -130,3 +136,37 @@ def test_decode_stack_graph_replay(gpu):
         torch.cuda.synchronize()
         assert torch.equal(x, ref)
         _ = (x0 * 2).sum().item()                    # eager work between replays
+
+
+def test_decode_stack_chunked_layers(gpu):
+    # 18 layers span two persistent launches (16 layers each at most); the
+    # second launch picks the residual stream up from the workspace.
+    bl = gpu
+    H, KV, F, D, n = 128, 64, 256, 32, 18
+    gl, rl = _build(bl, 21, n, H, KV, F)
+    x0 = workloads.stack_token(21, H)
+    x = x0.cuda()
+    trace = bl.bitlinear_decode_stack(gl, x, H, KV, F, D, trace=True,
+                                      path=bl.BL_STACK_PERSISTENT)
+    torch.cuda.synchronize()
+    ref_x, ref_trace = oracle.decode_stack(x0.numpy(), rl, H, KV, F, D, 1e-5)
+    _compare(trace.cpu().numpy(), ref_trace, H, KV)
+    err = np.abs(x.cpu().numpy().astype(np.float64) - ref_x).max()
+    assert err <= RTOL * np.abs(ref_x).max()
+
+
+def test_decode_stack_paths_agree_full_dims(gpu):
+    # Both paths on the 2B-class dimensions (3 layers): identical up to the
+    # order of the fp64 sum of H^2 in the subln RMS.
+    bl = gpu
+    H, KV, F, D = workloads.HIDDEN, workloads.KV, workloads.FFN, workloads.HEAD_DIM
+    gl, _ = _build(bl, 31, 3, H, KV, F)
+    x0 = workloads.stack_token(31, H).cuda()
+    xa, xb = x0.clone(), x0.clone()
+    ta = bl.bitlinear_decode_stack(gl, xa, H, KV, F, D, trace=True, path=bl.BL_STACK_LAUNCHES)
+    tb = bl.bitlinear_decode_stack(gl, xb, H, KV, F, D, trace=True,
+                                   path=bl.BL_STACK_PERSISTENT)
+    torch.cuda.synchronize()
+    _compare(tb.cpu().numpy(), ta.cpu().numpy().astype(np.float32), H, KV)
+    assert torch.isfinite(xb).all()
+    assert (xa - xb).abs().max().item() <= RTOL * xa.abs().max().item()
