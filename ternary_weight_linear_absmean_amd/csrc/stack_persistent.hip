@@ -41,6 +41,8 @@
 // time (only possible if the grid is not all resident) raises an error word,
 // fills x with NaN and leaves; the others then see the error word and leave.
 // The host launches at most one workgroup per compute unit.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -82,12 +84,21 @@ struct PArgs {
     float *trace;                             // row of this launch's first layer, or null
     int trace_stride;
     float *q, *k;                             // outputs nothing reads back
-    uint2 *xa, *xm, *v, *o, *h, *y;           // tagged (value bits, tag)
+    uint2 *xa, *xm, *v, *o, *h, *y;           // tagged (value bits, tag), slot 0
+    int slot_stride;                          // tagged values per layer slot
     unsigned *err;
 };
 
 // tag of the values produced in phase p of global layer lg (0 = cleared)
 __device__ __forceinline__ unsigned tag_of(int lg, int p) { return 4u * lg + p + 1u; }
+
+// Each of kMaxLayers layer slots has its own tagged vectors (layer lg uses
+// slot lg % kMaxLayers): within a launch no vector is written twice, so a
+// line that a consumer's L2 cached early is never mistaken later (its tag
+// would not match anyway; this keeps such misses rare).
+__device__ __forceinline__ uint2 *slot(const PArgs &a, uint2 *p, int lg) {
+    return p + (size_t)(lg % kMaxLayers) * a.slot_stride;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
@@ -239,14 +250,18 @@ __device__ __forceinline__ bool receive(const PArgs &a, const uint2 *p0, unsigne
                 return false;
         }
     }
-    while (pending) {
+    // One sweep through the L2 (plain loads: after the proxy most chunks are
+    // in memory, and the workgroups of an XCD then share one fetch of each
+    // line), then device-coherent re-polls of whatever is still stale.
+    auto sweep = [&](auto aux) {
+        constexpr int kAux = decltype(aux)::value;
         v4u w0[NC], w1[NC];
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             if (pending >> i & 1u) {
                 const int off = idx(2 * (r + i * kR)) * 8;
-                w0[i] = __builtin_amdgcn_raw_buffer_load_b128(r0, off, 0, kSC1);
-                if (TWO) w1[i] = __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, kSC1);
+                w0[i] = __builtin_amdgcn_raw_buffer_load_b128(r0, off, 0, kAux);
+                if (TWO) w1[i] = __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, kAux);
             }
         }
 #pragma unroll
@@ -258,6 +273,10 @@ __device__ __forceinline__ bool receive(const PArgs &a, const uint2 *p0, unsigne
                 pending &= ~(1u << i);
             }
         }
+    };
+    sweep(std::integral_constant<int, 0>{});
+    while (pending) {
+        sweep(std::integral_constant<int, kSC1>{});
         if (pending && (ld_u(a.err) != 0u ||
                         __builtin_amdgcn_s_memrealtime() - start > kTimeoutTicks))
             return false;
@@ -316,17 +335,18 @@ __device__ __forceinline__ bool receive_p0(const PArgs &a, Smem &sm, int lg, flo
             if (i < nj && c < K / 2) {
                 const float2 x = make_float2(__uint_as_float(w[i].x), __uint_as_float(w[i].y));
                 *reinterpret_cast<float2 *>(sm.vals + 2 * c) = x;
-                keep(a.xa, K, c, x, tag, tr);
+                keep(slot(a, a.xa, lg), K, c, x, tag, tr);
                 am = fmaxf(am, fmaxf(fabsf(x.x), fabsf(x.y)));
             }
         }
     } else {
-        ok = receive<kNH, true>(a, a.xm, tag_of(lg - 1, 2), a.y, tag_of(lg - 1, 3), K, K, Same{},
+        ok = receive<kNH, true>(a, slot(a, a.xm, lg - 1), tag_of(lg - 1, 2), slot(a, a.y, lg - 1),
+                                tag_of(lg - 1, 3), K, K, Same{},
                                 [&](int c, const v4u &m, const v4u &y) {
             const float2 mm = halves(m), yy = halves(y);
             const float2 x = make_float2(__fadd_rn(mm.x, yy.x), __fadd_rn(mm.y, yy.y));
             *reinterpret_cast<float2 *>(sm.vals + 2 * c) = x;
-            keep(a.xa, K, c, x, tag, tr);
+            keep(slot(a, a.xa, lg), K, c, x, tag, tr);
             am = fmaxf(am, fmaxf(fabsf(x.x), fabsf(x.y)));
         });
     }
@@ -338,7 +358,7 @@ __device__ __forceinline__ bool receive_p0(const PArgs &a, Smem &sm, int lg, flo
 // P1 input: a = v repeated per query group
 __device__ __forceinline__ bool receive_p1(const PArgs &a, Smem &sm, int lg) {
     float am = 0.0f;
-    const bool ok = receive<kNH, false>(a, a.v, tag_of(lg, 0), nullptr, 0u, a.KV, a.H,
+    const bool ok = receive<kNH, false>(a, slot(a, a.v, lg), tag_of(lg, 0), nullptr, 0u, a.KV, a.H,
                                         Expand{a.D, a.group},
                                         [&](int c, const v4u &w, const v4u &) {
         const float2 x = halves(w);
@@ -355,12 +375,13 @@ __device__ __forceinline__ bool receive_p2(const PArgs &a, Smem &sm, int lg, flo
     const int K = a.H;
     float am = 0.0f;
     const unsigned tag = tag_of(lg, 2);
-    const bool ok = receive<kNH, true>(a, a.xa, tag_of(lg, 0), a.o, tag_of(lg, 1), K, K, Same{},
+    const bool ok = receive<kNH, true>(a, slot(a, a.xa, lg), tag_of(lg, 0), slot(a, a.o, lg),
+                                       tag_of(lg, 1), K, K, Same{},
                                        [&](int c, const v4u &x, const v4u &o) {
         const float2 xx = halves(x), oo = halves(o);
         const float2 m = make_float2(__fadd_rn(xx.x, oo.x), __fadd_rn(xx.y, oo.y));
         *reinterpret_cast<float2 *>(sm.vals + 2 * c) = m;
-        keep(a.xm, K, c, m, tag, tr);
+        keep(slot(a, a.xm, lg), K, c, m, tag, tr);
         am = fmaxf(am, fmaxf(fabsf(m.x), fabsf(m.y)));
     });
     am = wave_max(am);
@@ -399,7 +420,7 @@ __device__ __forceinline__ bool receive_p3(const PArgs &a, Smem &sm, int lg, con
                 *reinterpret_cast<float2 *>(sm.gain + 2 * c) = make_float2(1.0f, 1.0f);
         }
     }
-    const bool ok = receive<kNF, false>(a, a.h, tag_of(lg, 2), nullptr, 0u, K, K, Same{},
+    const bool ok = receive<kNF, false>(a, slot(a, a.h, lg), tag_of(lg, 2), nullptr, 0u, K, K, Same{},
                                         [&](int c, const v4u &w, const v4u &) {
         *reinterpret_cast<float2 *>(sm.vals + 2 * c) = halves(w);
     });
@@ -533,7 +554,8 @@ __device__ __forceinline__ void receiver_loop(const PArgs &a, Smem &sm) {
     // the residual stream after the call's last layer: x = x_mid + y
     if (a.last && blockIdx.x == 0) {
         const int lg = a.l0 + a.n_layers - 1;
-        const bool ok = receive<kNH, true>(a, a.xm, tag_of(lg, 2), a.y, tag_of(lg, 3), H, H,
+        const bool ok = receive<kNH, true>(a, slot(a, a.xm, lg), tag_of(lg, 2), slot(a, a.y, lg),
+                                           tag_of(lg, 3), H, H,
                                            Same{}, [&](int c, const v4u &m, const v4u &y) {
             const float2 mm = halves(m), yy = halves(y);
             *reinterpret_cast<float2 *>(a.x_out + 2 * c) =
@@ -574,7 +596,7 @@ __device__ __forceinline__ void compute_loop(const PArgs &a, Smem &sm) {
                 a.k[gr - H] = y;
                 if (tr) tr[2 * H + gr - H] = y;
             } else {
-                st_tag(a.v + gr - H - KV, y, tag_of(lg, 0));
+                st_tag(slot(a, a.v, lg) + gr - H - KV, y, tag_of(lg, 0));
                 if (tr) tr[2 * H + KV + gr - H - KV] = y;
             }
         }
@@ -587,7 +609,7 @@ __device__ __forceinline__ void compute_loop(const PArgs &a, Smem &sm) {
         if (dot_phase<1>(a, sm, pre, ct, nr, acc0, acc1)) {
             const int gr = r0 + (ct >> a.lshift[1]);
             const float y = rescale(acc0, __fmul_rn(pre.g0, d));
-            st_tag(a.o + gr, y, tag_of(lg, 1));
+            st_tag(slot(a, a.o, lg) + gr, y, tag_of(lg, 1));
             if (tr) tr[2 * H + 2 * KV + gr] = y;
         }
         prefetch<2>(a, L, ct, pre);
@@ -601,7 +623,7 @@ __device__ __forceinline__ void compute_loop(const PArgs &a, Smem &sm) {
             const float G = rescale(acc0, __fmul_rn(pre.g0, d));
             const float U = rescale(acc1, __fmul_rn(pre.g1, d));
             const float r = G > 0.0f ? G : 0.0f;
-            st_tag(a.h + gr, __fmul_rn(__fmul_rn(r, r), U), tag_of(lg, 2));
+            st_tag(slot(a, a.h, lg) + gr, __fmul_rn(__fmul_rn(r, r), U), tag_of(lg, 2));
         }
         prefetch<3>(a, L, ct, pre);
 
@@ -616,7 +638,7 @@ __device__ __forceinline__ void compute_loop(const PArgs &a, Smem &sm) {
         if (dot_phase<3>(a, sm, pre, ct, nr, acc0, acc1)) {
             const int gr = r0 + (ct >> a.lshift[3]);
             const float y = rescale(acc0, __fmul_rn(pre.g0, d));
-            st_tag(a.y + gr, y, tag_of(lg, 3));
+            st_tag(slot(a, a.y, lg) + gr, y, tag_of(lg, 3));
             if (tr) tr[4 * H + 2 * KV + gr] = y;
         }
         if (l + 1 < a.n_layers) prefetch<0>(a, a.layer[l + 1], ct, pre);
@@ -680,8 +702,9 @@ bool plan(int G, int H, int KV, int F, int D, int (&ls)[4], int (&ns)[4]) {
 }  // namespace
 
 size_t stack_persistent_ws_floats(int H, int KV, int F) {
-    // tagged xa, xm, o, y [H], v [KV], h [F] (2 floats each), then err
-    return 2 * ((size_t)4 * H + KV + F) + 64;
+    // per layer slot tagged xa, xm, o, y [H], v [KV], h [F] (2 floats each),
+    // then err
+    return 2 * (size_t)kMaxLayers * (4 * (size_t)H + KV + F) + 64;
 }
 
 bool stack_persistent_fits(int H, int KV, int F, int D) {
@@ -702,9 +725,10 @@ hipError_t launch_decode_stack_persistent(const StackLayer *layers, int n_layers
     a.q = ws.q; a.k = ws.k;
     uint2 *t = reinterpret_cast<uint2 *>(ws.tagged);
     a.xa = t; a.xm = t + H; a.o = t + 2 * H; a.y = t + 3 * H; a.v = t + 4 * H; a.h = t + 4 * H + KV;
-    const int n_tagged = 4 * H + KV + F;
+    a.slot_stride = 4 * H + KV + F;
+    const int n_tagged = kMaxLayers * a.slot_stride;
     a.err = reinterpret_cast<unsigned *>(t + n_tagged);
-    hipLaunchKernelGGL(stack_reset_kernel, dim3(64), dim3(256), 0, s, t, n_tagged, a.err);
+    hipLaunchKernelGGL(stack_reset_kernel, dim3(256), dim3(256), 0, s, t, n_tagged, a.err);
     for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
         const int n = n_layers - l0 < kMaxLayers ? n_layers - l0 : kMaxLayers;
         for (int i = 0; i < n; ++i) {
