@@ -51,8 +51,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--part", default="all", choices=["all", "decode", "gemm", "ffn", "stack"],
-                    help="restrict the GPU legs (for profiling runs)")
+    ap.add_argument("--part", default="all", choices=["all", "decode", "gemm", "ffn", "stack", "copy"],
+                    help="restrict the GPU legs (for profiling runs); 'copy' (not in 'all') "
+                         "times a plain device copy of 256 MiB, the reference for the "
+                         "byte counters")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
@@ -290,6 +292,25 @@ def bench_stack(bl, torch, workloads, steps, warmup):
                                    launches_per_token=2 + 8 * L))
 
 
+def bench_copy(torch, steps):
+    """A plain device-to-device copy of 256 MiB: the kernel whose HBM byte
+    counters (FETCH_SIZE, WRITE_SIZE) calibrate the ones read for the GEMV."""
+    n = 256 * 2 ** 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * t0.elapsed_time(t1) / steps
+    return dict(bytes_read=n, bytes_written=n, us=round(us, 2), GBs=round(2 * n / us / 1e3, 1))
+
+
 def cpu_baseline(torch, workloads, seconds):
     """The oracle, as it stands, on the decode step's four shapes, repeated
     for about `seconds` of wall time."""
@@ -353,6 +374,8 @@ def main():
         out["gemm"] = bench_gemm(bl, torch, workloads, max(10, args.steps // 8), 5)
     if args.part in ("all", "ffn"):
         out["ffn"] = bench_ffn(bl, torch, workloads, max(5, args.steps // 40), 2)
+    if args.part == "copy":
+        out["copy"] = bench_copy(torch, 10)
     if args.part in ("all", "stack"):
         out["stack"] = bench_stack(bl, torch, workloads, max(20, args.steps // 4), 5)
     if not args.no_cpu and args.part == "all":

@@ -88,6 +88,14 @@ __device__ __forceinline__ int act_code(float x, float s) {
     return (int)r;
 }
 
+// A read-only value every lane reads from the same address, through the
+// constant address space: a scalar load.  It does not share the vector-memory
+// counter with weight loads and output stores, so issuing it early and using
+// it late never waits on those.
+__device__ __forceinline__ float scalar_load(const float *p) {
+    return *(const __attribute__((address_space(4))) float *)p;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

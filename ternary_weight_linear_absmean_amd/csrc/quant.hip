@@ -14,35 +14,48 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // gamma, step 1: fp64 sum of |W[n][k]| over k in ascending order, one row per
-// thread.  A wave stages a 64-row x 64-column tile through LDS with coalesced
-// float4 loads, then each thread adds its row's 64 values in k order.  Tail
-// columns are read as 0, and adding +0.0 to a non-negative sum is exact, so
-// the result is the plain ascending-k sum.
+// thread.  A wave stages a 64-row x 64-column tile through LDS (coalesced
+// float4 loads, 16 per thread), then each thread adds its row's 64 values in
+// k order.  The next tile's loads are all issued before the current tile is
+// summed, so memory latency overlaps the (inherently sequential) fp64 adds.
+// Tail columns are read as 0, and adding +0.0 to a non-negative sum is
+// exact, so the result is the plain ascending-k sum.
 constexpr int kRowsumRows = 64;
 constexpr int kRowsumCols = 64;
+constexpr int kRowsumLoads = kRowsumRows * (kRowsumCols / 4) / 64;   // float4 per thread
 
 __global__ __launch_bounds__(64) void rowsum_abs_kernel(const float *__restrict__ W, int64_t N,
                                                         int64_t K, double *__restrict__ rowsum) {
     __shared__ float tile[kRowsumRows][kRowsumCols + 1];
     const int t = threadIdx.x;
     const int64_t n0 = (int64_t)blockIdx.x * kRowsumRows;
+    // thread t's float4 i covers row (t + 64 i) / 16, columns 4 ((t + 64 i) % 16)..+3
+    auto load_tile = [&](int64_t k0, float4 (&v)[kRowsumLoads]) {
+#pragma unroll
+        for (int i = 0; i < kRowsumLoads; ++i) {
+            const int j = t + 64 * i;
+            const int64_t n = n0 + j / (kRowsumCols / 4);
+            const int64_t k = k0 + 4 * (j % (kRowsumCols / 4));
+            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (n < N && k < K)   // K % 4 == 0, so a float4 never straddles K
+                v[i] = *reinterpret_cast<const float4 *>(W + n * K + k);
+        }
+    };
+    float4 v[kRowsumLoads];
+    load_tile(0, v);
     double sum = 0.0;
     for (int64_t k0 = 0; k0 < K; k0 += kRowsumCols) {
-        // 64 rows x 16 float4 = 1024 float4, 16 per thread.
-        for (int i = t; i < kRowsumRows * (kRowsumCols / 4); i += 64) {
-            const int r = i / (kRowsumCols / 4);
-            const int c4 = i % (kRowsumCols / 4);
-            const int64_t n = n0 + r;
-            const int64_t k = k0 + 4 * c4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (n < N && k < K)   // K % 4 == 0, so a float4 never straddles K
-                v = *reinterpret_cast<const float4 *>(W + n * K + k);
-            tile[r][4 * c4 + 0] = v.x;
-            tile[r][4 * c4 + 1] = v.y;
-            tile[r][4 * c4 + 2] = v.z;
-            tile[r][4 * c4 + 3] = v.w;
+#pragma unroll
+        for (int i = 0; i < kRowsumLoads; ++i) {
+            const int j = t + 64 * i;
+            const int r = j / (kRowsumCols / 4), c = 4 * (j % (kRowsumCols / 4));
+            tile[r][c + 0] = v[i].x;
+            tile[r][c + 1] = v[i].y;
+            tile[r][c + 2] = v[i].z;
+            tile[r][c + 3] = v[i].w;
         }
         __syncthreads();
+        if (k0 + kRowsumCols < K) load_tile(k0 + kRowsumCols, v);
         for (int c = 0; c < kRowsumCols; ++c)
             sum += fabs((double)tile[t][c]);
         __syncthreads();
@@ -52,18 +65,30 @@ __global__ __launch_bounds__(64) void rowsum_abs_kernel(const float *__restrict_
         rowsum[n] = sum;
 }
 
-// gamma, step 2: add the row sums in ascending n (one wave; every lane forms
-// the same sequential sum from values broadcast lane by lane), divide by n in
-// fp64, round once to fp32.
+// gamma, step 2: add the row sums in ascending n, divide by n in fp64, round
+// once to fp32.  The wave stages chunks of row sums in LDS (all loads of a
+// chunk in flight together) and lane 0 adds them in order.
+constexpr int kGammaChunk = 2048;
+
 __global__ __launch_bounds__(64) void gamma_kernel(const double *__restrict__ rowsum, int64_t N,
                                                    int64_t K, float *__restrict__ gamma) {
+    __shared__ double buf[kGammaChunk];
     const int lane = threadIdx.x;
     double total = 0.0;
-    for (int64_t c = 0; c < N; c += 64) {
-        const double v = (c + lane < N) ? rowsum[c + lane] : 0.0;
-        const int cnt = (N - c) < 64 ? (int)(N - c) : 64;
-        for (int j = 0; j < cnt; ++j)
-            total += __shfl(v, j);
+    for (int64_t c0 = 0; c0 < N; c0 += kGammaChunk) {
+        const int cnt = (N - c0) < kGammaChunk ? (int)(N - c0) : kGammaChunk;
+        double v[kGammaChunk / 64];
+#pragma unroll
+        for (int i = 0; i < kGammaChunk / 64; ++i) {
+            const int j = lane + 64 * i;
+            v[i] = j < cnt ? rowsum[c0 + j] : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < kGammaChunk / 64; ++i) buf[lane + 64 * i] = v[i];
+        __syncthreads();
+        if (lane == 0)
+            for (int j = 0; j < cnt; ++j) total += buf[j];
+        __syncthreads();
     }
     if (lane == 0)   // mean of an empty tensor: gamma = 0
         gamma[0] = (N * K == 0) ? 0.0f : (float)(total / (double)(N * K));

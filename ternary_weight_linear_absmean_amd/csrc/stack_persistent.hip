@@ -159,13 +159,6 @@ __device__ __forceinline__ const uint4 *row_ptr(const PArgs &a, const PLayer &L,
     return reinterpret_cast<const uint4 *>(L.W[6] + (size_t)gr * rb);
 }
 
-// A gamma (read-only, the same for every lane) through the constant address
-// space: a scalar load, which does not share the vector-memory counter with
-// the weight loads and the output stores, so using it never waits on those.
-__device__ __forceinline__ float sload(const float *p) {
-    return *(const __attribute__((address_space(4))) float *)p;
-}
-
 // What a compute thread needs before the phase input arrives: its packed
 // weight units and the phase's gammas.
 struct Pre {
@@ -196,10 +189,10 @@ __device__ __forceinline__ void prefetch(const PArgs &a, const PLayer &L, int ct
             if (P == 2) pre.w[half + i] = second[u];
         }
     }
-    if (P == 0) { pre.g0 = sload(L.g[0]); pre.g1 = sload(L.g[1]); pre.g2 = sload(L.g[2]); }
-    if (P == 1) pre.g0 = sload(L.g[3]);
-    if (P == 2) { pre.g0 = sload(L.g[4]); pre.g1 = sload(L.g[5]); }
-    if (P == 3) pre.g0 = sload(L.g[6]);
+    if (P == 0) { pre.g0 = scalar_load(L.g[0]); pre.g1 = scalar_load(L.g[1]); pre.g2 = scalar_load(L.g[2]); }
+    if (P == 1) pre.g0 = scalar_load(L.g[3]);
+    if (P == 2) { pre.g0 = scalar_load(L.g[4]); pre.g1 = scalar_load(L.g[5]); }
+    if (P == 3) pre.g0 = scalar_load(L.g[6]);
 }
 
 struct Smem {
