@@ -39,6 +39,30 @@ I8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
 COLD_BYTES = 600 * 2 ** 20     # > 2 x 256 MB Infinity Cache
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_fused_decode_m1.md")
+GEMV_SOURCE = os.path.join(ROOT, "ternary_weight_linear_absmean_amd", "csrc", "gemv.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused decode kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (calibrated on a plain copy),
+    or None when that summary was taken on a different gemv.hip."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src = hashlib.sha256(open(GEMV_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line)
+    key = "source_sha256(ternary_weight_linear_absmean_amd/csrc/gemv.hip)"
+    if fields.get(key, "").strip() != src:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def decode_bytes(K, N):
     """Algorithmic bytes of one M = 1 BitLinear from bf16 activations: packed
     2-bit W + bf16 X + fp32 Y + gamma."""
@@ -363,7 +387,8 @@ def main():
         out["ms_per_step"] = round(dec["ms_per_step"], 5)
         out["roofline"] = {"bound": "hbm", "achieved": round(dec["achieved"], 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                           "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic(),
                            "kernel": "gemv_fused_kernel<1> (bitlinear_gemv_fused, 4 jobs, M=1)",
                            "avg_launch_us": round(dec["kernel_us"], 3),
                            "bytes_per_launch": dec["step_bytes"]}
