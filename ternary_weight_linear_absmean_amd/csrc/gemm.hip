@@ -118,11 +118,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 // ---------------------------------------------------------------------------
 // Large-M kernel on v_mfma_i32_32x32x32_i8 (on gfx950 the 32x32x32 int8 form
 // sustains about twice the throughput of 16x16x64 in a plain MFMA loop).
-// Workgroup = WM x WN waves, each wave owns 128 x 64 of Y = 4 x 2 blocks of
-// 32 x 32 (128 int32 accumulators per lane); tile = 128 WM x 64 WN.
-//   <2, 4>: 256 x 256 tiles, 512 threads (wide N, e.g. K2560 -> N6912)
-//   <1, 2>: 128 x 128 tiles, 128 threads (narrow N, e.g. K6912 -> N2560,
-//           where 256 x 256 tiles would leave most CUs idle)
+// Workgroup = WM x WN waves, each wave owns MI x NJ blocks of 32 x 32 of Y
+// (16 MI NJ int32 accumulators per lane); tile = 32 MI WM x 32 NJ WN.
+//   <2, 4, 4, 2>: 256 x 256 tiles, 512 threads (wide N, e.g. K2560 -> N6912)
+//   <2, 4, 2, 2>: 128 x 256 tiles, 512 threads (narrow N, e.g. K6912 -> N2560,
+//                 where 256 x 256 tiles would leave most CUs idle): measured
+//                 59 us on M2048 K6912 N2560 against 73 us for 128 x 128
 // k-step 128: the activation tile (transposed 16-byte groups, see
 // device_common.h) and the packed weight tile (2-bit codes, 4x smaller than
 // int8) are staged in LDS, double-buffered, from registers loaded two
@@ -139,7 +140,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 constexpr int BK2 = 128;
 constexpr int kAPitch = BK2 / 16 + 1;          // uint4 per A row (8 + 1 pad)
 constexpr int kBPitch = BK2 / 16 + 1;          // dwords per B column (8 + 1 pad)
-constexpr int MI2 = 4, NJ2 = 2;
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 template <int AG, int BG> struct Stage2 { uint4 a[AG]; uint4 b[BG]; };
@@ -188,12 +188,14 @@ __device__ __forceinline__ void store_stage2(const Stage2<AG, BG> &st, uint4 *As
     }
 }
 
-template <int WM, int WN>
+template <int WM, int WN, int MI2, int NJ2>
 __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
     float *__restrict__ Y, int32_t *__restrict__ acc_out, int m_tiles) {
-    constexpr int BM2 = 128 * WM, BN2 = 64 * WN, kThreads2 = 64 * WM * WN;
+    constexpr int BM2 = 32 * MI2 * WM, BN2 = 32 * NJ2 * WN, kThreads2 = 64 * WM * WN;
+    static_assert(BM2 * 8 % kThreads2 == 0 && BN2 * 2 % kThreads2 == 0,
+                  "every thread stages whole 16-byte groups of A and B");
     constexpr int AG = BM2 * 8 / kThreads2, BG = BN2 * 2 / kThreads2;
     constexpr int kStageA = BM2 * kAPitch, kStageB = BN2 * kBPitch;
     __shared__ uint4 As[2 * kStageA];
@@ -210,45 +212,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
 #pragma unroll
         for (int j = 0; j < NJ2; ++j) acc[i][j] = v16i{};
     const SrcPtr<AG, BG> sp = src_ptrs<BM2, BN2, kThreads2, AG, BG>(Xq, Wp, M, N, K, KB, m_base, n_base, tid);
-    const int a_off = (wm * 128 + (lane & 31)) * kAPitch + (lane >> 5);
-    const int b_off = (wn * 64 + (lane & 31)) * kBPitch + (lane >> 5);
-    Stage2<AG, BG> s0, s1;
-    if (KT > 0) load_stage2(s0, sp, 0);
-    if (KT > 1) load_stage2(s1, sp, BK2);
-    if (KT > 0) store_stage2<kThreads2>(s0, As, Bs, tid);
-    __syncthreads();
+    const int a_off = (wm * 32 * MI2 + (lane & 31)) * kAPitch + (lane >> 5);
+    const int b_off = (wn * 32 * NJ2 + (lane & 31)) * kBPitch + (lane >> 5);
+    // The loads for k-step kt + 2 are issued on every step, past the end
+    // from the last k-step again (a valid address, never stored to LDS):
+    // with no branch around them the compiler counts exactly five loads
+    // in flight behind the stage it stores, and waits for that stage only
+    // instead of draining everything issued this step.
+    const int kt_last = KT - 1;
+    if (KT > 0) {
+        Stage2<AG, BG> s0, s1;
+        load_stage2(s0, sp, 0);
+        load_stage2(s1, sp, min(1, kt_last) * BK2);
+        store_stage2<kThreads2>(s0, As, Bs, tid);
+        __syncthreads();
 #define BL_STEP(KT_, MINE, NEXT)                                                              \
-    {                                                                                         \
-        const int kt_ = (KT_);                                                                \
-        if (kt_ + 2 < KT) load_stage2(MINE, sp, (kt_ + 2) * BK2);                             \
-        const int buf = kt_ & 1;                                                              \
-        __builtin_amdgcn_iglp_opt(1);                                                       \
-        const uint4 *A = As + buf * kStageA + a_off;                                          \
-        const uint32_t *B = Bs + buf * kStageB + b_off;                                       \
-        _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                       \
-            v4i bf[NJ2];                                                                      \
-            _Pragma("unroll") for (int j = 0; j < NJ2; ++j) {                                 \
-                uint4 v;                                                                      \
-                unpack16(B[j * 32 * kBPitch + 2 * h], v.x, v.y, v.z, v.w);                    \
-                bf[j] = as_v4i(v);                                                            \
-            }                                                                                 \
-            v4i af[MI2];                                                                      \
-            _Pragma("unroll") for (int i = 0; i < MI2; ++i)                                   \
-                af[i] = as_v4i(A[i * 32 * kAPitch + 2 * h]);                                  \
-            _Pragma("unroll") for (int i = 0; i < MI2; ++i)                                   \
-                _Pragma("unroll") for (int j = 0; j < NJ2; ++j)                               \
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0); \
-        }                                                                                     \
-        if (kt_ + 1 < KT) store_stage2<kThreads2>(NEXT, As + (buf ^ 1) * kStageA, Bs + (buf ^ 1) * kStageB, tid); \
-        __syncthreads();                                                                      \
+        {                                                                                         \
+            const int kt_ = (KT_);                                                                \
+            load_stage2(MINE, sp, min(kt_ + 2, kt_last) * BK2);                                   \
+            const int buf = kt_ & 1;                                                              \
+            __builtin_amdgcn_iglp_opt(1);                                                       \
+            const uint4 *A = As + buf * kStageA + a_off;                                          \
+            const uint32_t *B = Bs + buf * kStageB + b_off;                                       \
+            _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                       \
+                v4i bf[NJ2];                                                                      \
+                _Pragma("unroll") for (int j = 0; j < NJ2; ++j) {                                 \
+                    uint4 v;                                                                      \
+                    unpack16(B[j * 32 * kBPitch + 2 * h], v.x, v.y, v.z, v.w);                    \
+                    bf[j] = as_v4i(v);                                                            \
+                }                                                                                 \
+                v4i af[MI2];                                                                      \
+                _Pragma("unroll") for (int i = 0; i < MI2; ++i)                                   \
+                    af[i] = as_v4i(A[i * 32 * kAPitch + 2 * h]);                                  \
+                _Pragma("unroll") for (int i = 0; i < MI2; ++i)                                   \
+                    _Pragma("unroll") for (int j = 0; j < NJ2; ++j)                               \
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0); \
+            }                                                                                     \
+            if (kt_ + 1 < KT) store_stage2<kThreads2>(NEXT, As + (buf ^ 1) * kStageA, Bs + (buf ^ 1) * kStageB, tid); \
+            __syncthreads();                                                                      \
+        }
+        int kt = 0;
+    #pragma unroll 1
+        for (; kt + 2 <= KT; kt += 2) {
+            BL_STEP(kt, s0, s1)
+            BL_STEP(kt + 1, s1, s0)
+        }
+        if (kt < KT) BL_STEP(kt, s0, s1)
     }
-    int kt = 0;
-#pragma unroll 1
-    for (; kt + 2 <= KT; kt += 2) {
-        BL_STEP(kt, s0, s1)
-        BL_STEP(kt + 1, s1, s0)
-    }
-    if (kt < KT) BL_STEP(kt, s0, s1)
 #undef BL_STEP
     // K % 128 == 64: one last 64-wide half step straight from global memory
     if (K % BK2) {
@@ -292,12 +302,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     for (int i = 0; i < MI2; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = m_base + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = m_base + wm * 32 * MI2 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if (row >= M) continue;
             const float c = __fmul_rn(g, d[row]);
 #pragma unroll
             for (int j = 0; j < NJ2; ++j) {
-                const int col = n_base + wn * 64 + j * 32 + (lane & 31);
+                const int col = n_base + wn * 32 * NJ2 + j * 32 + (lane & 31);
                 if (col < N) {
                     const size_t o = (size_t)row * N + col;
                     Y[o] = rescale(acc[i][j][r], c);
@@ -322,16 +332,12 @@ hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *W
 #endif
         if (cfg == 0) {
             const int m_tiles = (M + 255) / 256, n_tiles = (N + 255) / 256;
-            hipLaunchKernelGGL((gemm256_kernel<2, 4>), dim3(m_tiles * n_tiles), dim3(512), 0, s, Xq, d,
-                               M, Wp, gamma, N, K, Y, acc, m_tiles);
-        } else if (cfg == 1) {
-            const int m_tiles = (M + 127) / 128, n_tiles = (N + 127) / 128;
-            hipLaunchKernelGGL((gemm256_kernel<1, 2>), dim3(m_tiles * n_tiles), dim3(128), 0, s, Xq, d,
-                               M, Wp, gamma, N, K, Y, acc, m_tiles);
+            hipLaunchKernelGGL((gemm256_kernel<2, 4, 4, 2>), dim3(m_tiles * n_tiles), dim3(512), 0,
+                               s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles);
         } else {
-            const int m_tiles = (M + 255) / 256, n_tiles = (N + 127) / 128;
-            hipLaunchKernelGGL((gemm256_kernel<2, 2>), dim3(m_tiles * n_tiles), dim3(256), 0, s, Xq, d,
-                               M, Wp, gamma, N, K, Y, acc, m_tiles);
+            const int m_tiles = (M + 127) / 128, n_tiles = (N + 255) / 256;
+            hipLaunchKernelGGL((gemm256_kernel<2, 4, 2, 2>), dim3(m_tiles * n_tiles), dim3(512), 0,
+                               s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles);
         }
         return hipGetLastError();
     }
