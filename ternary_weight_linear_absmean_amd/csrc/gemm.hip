@@ -200,6 +200,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     constexpr int kStageA = BM2 * kAPitch, kStageB = BN2 * kBPitch;
     __shared__ uint4 As[2 * kStageA];
     __shared__ uint32_t Bs[2 * kStageB];
+    __shared__ float cS[BM2];                  // fl(gamma * d[row]) of the tile's rows
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int m_base = (blockIdx.x % m_tiles) * BM2;
@@ -219,11 +220,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     // with no branch around them the compiler counts exactly five loads
     // in flight behind the stage it stores, and waits for that stage only
     // instead of draining everything issued this step.
+    // The row factors are read once, ahead of the operand loads, and kept in
+    // LDS: the epilogue then issues no global load, so its stores never wait
+    // behind one (the vector-memory counter retires loads and stores in order).
+    float d_row[(BM2 + kThreads2 - 1) / kThreads2];
+#pragma unroll
+    for (int t = 0; t * kThreads2 < BM2; ++t)
+        if (t * kThreads2 + tid < BM2) d_row[t] = d[min(m_base + t * kThreads2 + tid, M - 1)];
+    const float g = scalar_load(gamma);
     const int kt_last = KT - 1;
     if (KT > 0) {
         Stage2<AG, BG> s0, s1;
         load_stage2(s0, sp, 0);
         load_stage2(s1, sp, min(1, kt_last) * BK2);
+#pragma unroll
+        for (int t = 0; t * kThreads2 < BM2; ++t)
+            if (t * kThreads2 + tid < BM2) cS[t * kThreads2 + tid] = __fmul_rn(g, d_row[t]);
         store_stage2<kThreads2>(s0, As, Bs, tid);
         __syncthreads();
 #define BL_STEP(KT_, MINE, NEXT)                                                              \
@@ -252,7 +264,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
             __syncthreads();                                                                      \
         }
         int kt = 0;
-    #pragma unroll 1
+#pragma unroll 1
         for (; kt + 2 <= KT; kt += 2) {
             BL_STEP(kt, s0, s1)
             BL_STEP(kt + 1, s1, s0)
@@ -260,6 +272,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
         if (kt < KT) BL_STEP(kt, s0, s1)
     }
 #undef BL_STEP
+    if (KT == 0) {                             // K < 128: no prologue ran
+#pragma unroll
+        for (int t = 0; t * kThreads2 < BM2; ++t)
+            if (t * kThreads2 + tid < BM2) cS[t * kThreads2 + tid] = __fmul_rn(g, d_row[t]);
+        __syncthreads();
+    }
     // K % 128 == 64: one last 64-wide half step straight from global memory
     if (K % BK2) {
         const int k0 = KT * BK2;
@@ -297,14 +315,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
         }
     }
 
-    const float g = gamma[0];
+    // Whole tile inside Y and no int32 copy: branch-free stores from one
+    // per-lane base pointer (row offsets are uniform multiples of N).
+    if (!acc_out && m_base + BM2 <= M && n_base + BN2 <= N) {
+        float *yl = Y + (size_t)(m_base + wm * 32 * MI2 + 4 * (lane >> 5)) * N +
+                    (n_base + wn * 32 * NJ2 + (lane & 31));
+        const float *cl = cS + wm * 32 * MI2 + 4 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < MI2; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = i * 32 + 8 * (r >> 2) + (r & 3);
+                const float c = cl[lr];
+                float *y = yl + (size_t)lr * N;
+#pragma unroll
+                for (int j = 0; j < NJ2; ++j) y[j * 32] = rescale(acc[i][j][r], c);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MI2; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = m_base + wm * 32 * MI2 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int lrow = wm * 32 * MI2 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = m_base + lrow;
             if (row >= M) continue;
-            const float c = __fmul_rn(g, d[row]);
+            const float c = cS[lrow];
 #pragma unroll
             for (int j = 0; j < NJ2; ++j) {
                 const int col = n_base + wn * 32 * NJ2 + j * 32 + (lane & 31);
