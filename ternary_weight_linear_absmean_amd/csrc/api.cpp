@@ -75,6 +75,9 @@ constexpr int64_t kI32Max = 2147483647;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // FFN workspace: G [M][F] f32 | U [M][F] f32 | Hq [M][F] i8 | dh [M] f32 | dz [M] f32.
+// With the fused gate/up kernel (gated, M >= 128) G holds Z and U's region the
+// per-tile row partials: max |Z| f32 [M][T] then, 256-byte aligned, sum H^2
+// f64 [M][T], T = ceil(F / 128); 12 T <= 4 F bytes per row for any F >= 64.
 struct FfnWs {
     size_t g, u, hq, dh, dz, total;
 };
@@ -322,11 +325,23 @@ BL_EXPORT bl_status bitlinear_ffn_relu2(const int8_t *Xq, const float *d, int64_
     float *dz = reinterpret_cast<float *>(base + w.dz);
     const int m = (int)M, k = (int)K, f = (int)F, n = (int)N;
 
-    hipError_t e = bl::launch_bitlinear(Xq, d, m, Wg, gamma_g, f, k, G, nullptr, s);
-    if (e == hipSuccess && Wu)
-        e = bl::launch_bitlinear(Xq, d, m, Wu, gamma_u, f, k, U, nullptr, s);
-    if (e == hipSuccess)
-        e = bl::launch_ffn_tail(G, U, norm_w, eps, m, f, hq, dhb, dz, s);
+    hipError_t e;
+    if (Wu && m >= 128) {
+        // one MFMA kernel for gate and up with the ReLU^2 product, gain and
+        // row partials in its epilogue; Z takes G's region, the partials U's
+        const int tiles = bl::ffn_gate_up_tiles(f);
+        float *pmax = reinterpret_cast<float *>(base + w.u);
+        double *psum = reinterpret_cast<double *>(base + w.u + round_up((size_t)M * tiles * 4, 256));
+        e = bl::launch_ffn_gate_up(Xq, d, m, k, Wg, gamma_g, Wu, gamma_u, norm_w, f, G, pmax, psum, s);
+        if (e == hipSuccess)
+            e = bl::launch_ffn_tail_z(G, pmax, psum, tiles, eps, m, f, hq, dhb, dz, s);
+    } else {
+        e = bl::launch_bitlinear(Xq, d, m, Wg, gamma_g, f, k, G, nullptr, s);
+        if (e == hipSuccess && Wu)
+            e = bl::launch_bitlinear(Xq, d, m, Wu, gamma_u, f, k, U, nullptr, s);
+        if (e == hipSuccess)
+            e = bl::launch_ffn_tail(G, U, norm_w, eps, m, f, hq, dhb, dz, s);
+    }
     if (e == hipSuccess && n > 0)
         e = bl::launch_bitlinear(hq, dz, m, Wd, gamma_d, n, f, Y, nullptr, s);
     return launched(e, name);

@@ -95,6 +95,9 @@ __device__ __forceinline__ int act_code(float x, float s) {
 __device__ __forceinline__ float scalar_load(const float *p) {
     return *(const __attribute__((address_space(4))) float *)p;
 }
+__device__ __forceinline__ double scalar_load(const double *p) {
+    return *(const __attribute__((address_space(4))) double *)p;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -98,7 +98,56 @@ __global__ __launch_bounds__(kThreads) void ffn_tail_kernel(
     }
 }
 
+// Tail after the fused gate/up kernel (M >= 128): Z = fl(H * g) is already
+// in memory and the gate/up epilogue left, per row and 128-column tile,
+// max |Z| and the fp64 sum of H^2.  One workgroup per row reduces those
+// partials in tile order (the same order in every thread, uniform addresses),
+// so max |Z| is exact and the sum is run-to-run identical; then it writes the
+// int8 codes of Z.  Z is read once, with non-temporal loads.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void ffn_tail_z_kernel(
+    const float *__restrict__ Z, const float *__restrict__ pmax, const double *__restrict__ psum,
+    int tiles, float eps, int F, int8_t *__restrict__ Hq, float *__restrict__ dh,
+    float *__restrict__ dz) {
+    const int64_t m = blockIdx.x;
+    float a = 0.0f;
+    double ss = 0.0;
+    for (int t = 0; t < tiles; ++t) {
+        a = fmaxf(a, scalar_load(pmax + m * tiles + t));
+        ss += scalar_load(psum + m * tiles + t);
+    }
+    const bool zero = !(a > 0.0f);
+    const float s = act_inv_scale(a);
+    const float *z_row = Z + m * F;
+    int8_t *q_row = Hq + m * F;
+    for (int f = 4 * threadIdx.x; f < F; f += 4 * kThreads) {     // F % 64 == 0
+        const f32x4 z = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(z_row + f));
+        const uint32_t q = (uint32_t)(act_code(z.x, s) & 0xFF) |
+                           ((uint32_t)(act_code(z.y, s) & 0xFF) << 8) |
+                           ((uint32_t)(act_code(z.z, s) & 0xFF) << 16) |
+                           ((uint32_t)(act_code(z.w, s) & 0xFF) << 24);
+        *reinterpret_cast<uint32_t *>(q_row + f) = q;
+    }
+    if (threadIdx.x == 0) {
+        const float dhm = act_scale(a);
+        dh[m] = dhm;
+        // a row whose Z is all zero has zero codes and scale 0
+        dz[m] = zero ? 0.0f : (float)((double)dhm / sqrt(ss / (double)F + (double)eps));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ffn_tail_z(const float *Z, const float *pmax, const double *psum, int tiles,
+                             float eps, int M, int F, int8_t *Hq, float *dh, float *dz,
+                             hipStream_t s) {
+    if (M == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(ffn_tail_z_kernel, dim3(M), dim3(kThreads), 0, s, Z, pmax, psum, tiles,
+                       eps, F, Hq, dh, dz);
+    return hipGetLastError();
+}
 
 hipError_t launch_ffn_tail(const float *G, const float *U, const float *norm_w, float eps,
                            int M, int F, int8_t *Hq, float *dh, float *dz, hipStream_t s) {

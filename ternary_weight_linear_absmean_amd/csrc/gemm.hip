@@ -166,6 +166,36 @@ __device__ __forceinline__ SrcPtr<AG, BG> src_ptrs(const int8_t *__restrict__ Xq
     }
     return p;
 }
+// Gate/up mode (the FFN block's first two BitLinears in one kernel).  The
+// B tile's 256 columns interleave the two weights in 32-row blocks: LDS
+// column b belongs to wave b / 64, block j = (b / 32) % 2 takes W_gate
+// (j = 0) or W_up (j = 1), row f = f0 + 32 (b / 64) + b % 32.  A wave's two
+// accumulator blocks then hold the gate and the up sums of the same 128 x 32
+// outputs in the same registers, and the epilogue forms
+// H = relu(G)^2 * U and Z = H * g without leaving the lane.
+struct GateUp {
+    const uint8_t *Wu;
+    const float *gamma_u;
+    const float *norm_w;     // [F] or null (ones)
+    float *Z;                // [M][F] fp32
+    float *pmax;             // [M][n_tiles]: max |Z| over the tile's columns
+    double *psum;            // [M][n_tiles]: sum of H^2 over the tile's columns
+    int n_tiles;
+};
+
+template <int BN, int T, int AG, int BG>
+__device__ __forceinline__ void gate_up_b_ptrs(SrcPtr<AG, BG> &p, const uint8_t *__restrict__ Wg,
+        const uint8_t *__restrict__ Wu, int F, int KB, int f0, int tid) {
+    static_assert(BN == 256, "gate/up tiles are 256 B-columns wide");
+#pragma unroll
+    for (int i = 0; i < BG; ++i) {
+        const int idx = tid + T * i;
+        const int b = idx >> 1;
+        const int f = min(f0 + 32 * (b >> 6) + (b & 31), F - 1);
+        p.b[i] = ((b >> 5) & 1 ? Wu : Wg) + (size_t)f * KB + 16 * (idx & 1);
+    }
+}
+
 template <int AG, int BG>
 __device__ __forceinline__ void load_stage2(Stage2<AG, BG> &st, const SrcPtr<AG, BG> &sp, int k0) {
 #pragma unroll
@@ -188,23 +218,99 @@ __device__ __forceinline__ void store_stage2(const Stage2<AG, BG> &st, uint4 *As
     }
 }
 
-template <int WM, int WN, int MI2, int NJ2>
+// Gate/up epilogue.  Each lane turns its gate / up sums into
+// G = fl(acc_g * fl(gamma_g d)), U = fl(acc_u * fl(gamma_u d)) and
+// H = fl(fl(relu(G)^2) * U), exactly as two separate products and the tail
+// would, and parks H in LDS.  Then every wave takes 32 rows, two per step:
+// a lane owns 4 consecutive columns, forms Z = fl(H * g), stores 16 bytes of
+// Z (a wave store covers two whole 512-byte row segments), and the 32 lanes
+// of a row reduce max |Z| and the fp64 sum of H^2 over the tile's columns in
+// a fixed order (4 terms per lane, then a butterfly), so a partial depends
+// only on the data.
+template <int WM, int MI2, int BM2, int BNO, int kHPitch>
+__device__ __forceinline__ void gate_up_epilogue(const v16i (&acc)[MI2][2], float *hS,
+        const float *cS, const float *cSu, const GateUp &gu, int M, int F, int m_base, int f0,
+        int wm, int wn, int lane, int wave) {
+    static_assert(BNO == 128 && BM2 == 32 * (WM * 4), "one 32-row band per wave in pass 2");
+    __syncthreads();                           // every wave is done with the operand stages
+#pragma unroll
+    for (int i = 0; i < MI2; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int lrow = wm * 32 * MI2 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const float G = rescale(acc[i][0][r], cS[lrow]);
+            const float U = rescale(acc[i][1][r], cSu[lrow]);
+            const float rg = G > 0.0f ? G : 0.0f;
+            hS[lrow * kHPitch + wn * 32 + (lane & 31)] = __fmul_rn(__fmul_rn(rg, rg), U);
+        }
+    }
+    __syncthreads();
+    const int c4 = 4 * (lane & 31);            // this lane's 4 columns of the tile
+    const bool col_ok = f0 + c4 < F;           // F % 64 == 0: 4 columns are all in or all out
+    float4 gain = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (gu.norm_w && col_ok) gain = *reinterpret_cast<const float4 *>(gu.norm_w + f0 + c4);
+    const int nt = (int)(f0 / BNO);
+#pragma unroll 2
+    for (int k = 0; k < 16; ++k) {
+        const int lrow = 32 * wave + 2 * k + (lane >> 5);
+        const int row = m_base + lrow;
+        const float4 h = *reinterpret_cast<const float4 *>(hS + lrow * kHPitch + c4);
+        float4 z;
+        z.x = __fmul_rn(h.x, gain.x);
+        z.y = __fmul_rn(h.y, gain.y);
+        z.z = __fmul_rn(h.z, gain.z);
+        z.w = __fmul_rn(h.w, gain.w);
+        const bool ok = col_ok && row < M;
+        float a = 0.0f;
+        double ss = 0.0;
+        if (ok) {
+            *reinterpret_cast<float4 *>(gu.Z + (size_t)row * F + f0 + c4) = z;
+            a = fmaxf(fmaxf(fabsf(z.x), fabsf(z.y)), fmaxf(fabsf(z.z), fabsf(z.w)));
+            ss = (double)h.x * h.x;
+            ss += (double)h.y * h.y;
+            ss += (double)h.z * h.z;
+            ss += (double)h.w * h.w;
+        }
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) {
+            a = fmaxf(a, __shfl_xor(a, off));
+            ss += __shfl_xor(ss, off);
+        }
+        if ((lane & 31) == 0 && row < M) {
+            gu.pmax[(size_t)row * gu.n_tiles + nt] = a;
+            gu.psum[(size_t)row * gu.n_tiles + nt] = ss;
+        }
+    }
+}
+
+template <int WM, int WN, int MI2, int NJ2, bool GU>
 __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
-    float *__restrict__ Y, int32_t *__restrict__ acc_out, int m_tiles) {
+    float *__restrict__ Y, int32_t *__restrict__ acc_out, int m_tiles, const GateUp gu) {
     constexpr int BM2 = 32 * MI2 * WM, BN2 = 32 * NJ2 * WN, kThreads2 = 64 * WM * WN;
     static_assert(BM2 * 8 % kThreads2 == 0 && BN2 * 2 % kThreads2 == 0,
                   "every thread stages whole 16-byte groups of A and B");
+    static_assert(!GU || (NJ2 == 2 && WN == 4),
+                  "gate/up mode: 4 waves across, one gate and one up block each");
     constexpr int AG = BM2 * 8 / kThreads2, BG = BN2 * 2 / kThreads2;
     constexpr int kStageA = BM2 * kAPitch, kStageB = BN2 * kBPitch;
-    __shared__ uint4 As[2 * kStageA];
-    __shared__ uint32_t Bs[2 * kStageB];
+    constexpr int BNO = GU ? BN2 / 2 : BN2;    // output columns of a tile
+    // LDS: the double-buffered operand stages; in gate/up mode the epilogue
+    // reuses the same bytes for the tile's H values [BM2][BNO + 8].
+    constexpr int kHPitch = BNO + 8;
+    constexpr int kMainBytes = 2 * kStageA * 16 + 2 * kStageB * 4;
+    constexpr int kEpiBytes = GU ? BM2 * kHPitch * 4 : 0;
+    constexpr int kLdsBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
+    __shared__ uint4 smem[kLdsBytes / 16];
+    uint4 *const As = smem;
+    uint32_t *const Bs = reinterpret_cast<uint32_t *>(smem + 2 * kStageA);
     __shared__ float cS[BM2];                  // fl(gamma * d[row]) of the tile's rows
+    __shared__ float cSu[GU ? BM2 : 1];        // fl(gamma_u * d[row]) (gate/up mode)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int m_base = (blockIdx.x % m_tiles) * BM2;
-    const int n_base = (blockIdx.x / m_tiles) * BN2;
+    const int n_base = (blockIdx.x / m_tiles) * BNO;
     const int KB = K / 4;
     const int KT = K / BK2;                    // full 128-wide steps
     v16i acc[MI2][NJ2];
@@ -212,7 +318,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     for (int i = 0; i < MI2; ++i)
 #pragma unroll
         for (int j = 0; j < NJ2; ++j) acc[i][j] = v16i{};
-    const SrcPtr<AG, BG> sp = src_ptrs<BM2, BN2, kThreads2, AG, BG>(Xq, Wp, M, N, K, KB, m_base, n_base, tid);
+    SrcPtr<AG, BG> sp = src_ptrs<BM2, BN2, kThreads2, AG, BG>(Xq, Wp, M, N, K, KB, m_base, n_base, tid);
+    if constexpr (GU) gate_up_b_ptrs<BN2, kThreads2, AG, BG>(sp, Wp, gu.Wu, N, KB, n_base, tid);
     const int a_off = (wm * 32 * MI2 + (lane & 31)) * kAPitch + (lane >> 5);
     const int b_off = (wn * 32 * NJ2 + (lane & 31)) * kBPitch + (lane >> 5);
     // The loads for k-step kt + 2 are issued on every step, past the end
@@ -228,14 +335,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     for (int t = 0; t * kThreads2 < BM2; ++t)
         if (t * kThreads2 + tid < BM2) d_row[t] = d[min(m_base + t * kThreads2 + tid, M - 1)];
     const float g = scalar_load(gamma);
+    const float gu_scale = GU ? scalar_load(gu.gamma_u) : 0.0f;
+    auto put_row_factors = [&]() {
+#pragma unroll
+        for (int t = 0; t * kThreads2 < BM2; ++t)
+            if (t * kThreads2 + tid < BM2) {
+                cS[t * kThreads2 + tid] = __fmul_rn(g, d_row[t]);
+                if constexpr (GU) cSu[t * kThreads2 + tid] = __fmul_rn(gu_scale, d_row[t]);
+            }
+    };
     const int kt_last = KT - 1;
     if (KT > 0) {
         Stage2<AG, BG> s0, s1;
         load_stage2(s0, sp, 0);
         load_stage2(s1, sp, min(1, kt_last) * BK2);
-#pragma unroll
-        for (int t = 0; t * kThreads2 < BM2; ++t)
-            if (t * kThreads2 + tid < BM2) cS[t * kThreads2 + tid] = __fmul_rn(g, d_row[t]);
+        put_row_factors();
         store_stage2<kThreads2>(s0, As, Bs, tid);
         __syncthreads();
 #define BL_STEP(KT_, MINE, NEXT)                                                              \
@@ -273,9 +387,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     }
 #undef BL_STEP
     if (KT == 0) {                             // K < 128: no prologue ran
-#pragma unroll
-        for (int t = 0; t * kThreads2 < BM2; ++t)
-            if (t * kThreads2 + tid < BM2) cS[t * kThreads2 + tid] = __fmul_rn(g, d_row[t]);
+        put_row_factors();
         __syncthreads();
     }
     // K % 128 == 64: one last 64-wide half step straight from global memory
@@ -315,6 +427,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
         }
     }
 
+    if constexpr (GU) {
+        gate_up_epilogue<WM, MI2, BM2, BNO, kHPitch>(acc, reinterpret_cast<float *>(smem), cS, cSu,
+                                                    gu, M, N, m_base, n_base, wm, wn, lane, wave);
+        return;
+    }
     // Whole tile inside Y and no int32 copy: branch-free stores from one
     // per-lane base pointer (row offsets are uniform multiples of N).
     if (!acc_out && m_base + BM2 <= M && n_base + BN2 <= N) {
@@ -369,17 +486,30 @@ hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *W
 #endif
         if (cfg == 0) {
             const int m_tiles = (M + 255) / 256, n_tiles = (N + 255) / 256;
-            hipLaunchKernelGGL((gemm256_kernel<2, 4, 4, 2>), dim3(m_tiles * n_tiles), dim3(512), 0,
-                               s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles);
+            hipLaunchKernelGGL((gemm256_kernel<2, 4, 4, 2, false>), dim3(m_tiles * n_tiles), dim3(512), 0,
+                               s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles, GateUp{});
         } else {
             const int m_tiles = (M + 127) / 128, n_tiles = (N + 255) / 256;
-            hipLaunchKernelGGL((gemm256_kernel<2, 4, 2, 2>), dim3(m_tiles * n_tiles), dim3(512), 0,
-                               s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles);
+            hipLaunchKernelGGL((gemm256_kernel<2, 4, 2, 2, false>), dim3(m_tiles * n_tiles), dim3(512), 0,
+                               s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles, GateUp{});
         }
         return hipGetLastError();
     }
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, Xq, d, M, Wp, gamma, N, K, Y, acc);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_gate_up(const int8_t *Xq, const float *d, int M, int K, const uint8_t *Wg,
+                              const float *gamma_g, const uint8_t *Wu, const float *gamma_u,
+                              const float *norm_w, int F, float *Z, float *pmax, double *psum,
+                              hipStream_t s) {
+    if (M == 0 || F == 0)
+        return hipSuccess;
+    const int m_tiles = (M + 255) / 256, n_tiles = ffn_gate_up_tiles(F);
+    const GateUp gu{Wu, gamma_u, norm_w, Z, pmax, psum, n_tiles};
+    hipLaunchKernelGGL((gemm256_kernel<2, 4, 4, 2, true>), dim3(m_tiles * n_tiles), dim3(512), 0, s,
+                       Xq, d, M, Wg, gamma_g, F, K, nullptr, nullptr, m_tiles, gu);
     return hipGetLastError();
 }
 

@@ -58,6 +58,19 @@ constexpr size_t kFusedMaxLds = 128 * 1024;
 // fused_lds_bytes(fused_tile(M), K, esize) <= kFusedMaxLds for every job.
 hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t s);
 
+// FFN block, M >= 128 with a gate: both first BitLinears in one MFMA kernel
+// (gemm.hip) whose epilogue writes Z = fl(fl(relu(G)^2 * U) * g) [M][F] and,
+// per row and 128-column tile, max |Z| and the fp64 sum of H^2 ([M][tiles]);
+// then the tail (ffn.hip) reduces the partials and writes the int8 codes.
+constexpr int ffn_gate_up_tiles(int F) { return (F + 127) / 128; }
+hipError_t launch_ffn_gate_up(const int8_t *Xq, const float *d, int M, int K, const uint8_t *Wg,
+                              const float *gamma_g, const uint8_t *Wu, const float *gamma_u,
+                              const float *norm_w, int F, float *Z, float *pmax, double *psum,
+                              hipStream_t s);
+hipError_t launch_ffn_tail_z(const float *Z, const float *pmax, const double *psum, int tiles,
+                             float eps, int M, int F, int8_t *Hq, float *dh, float *dz,
+                             hipStream_t s);
+
 // Picks the VALU kernel for M <= kGemvMaxTokens and MFMA otherwise.
 hipError_t launch_bitlinear(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                             const float *gamma, int N, int K, float *Y, int32_t *acc,

@@ -274,6 +274,38 @@ def test_ffn_prefill_full_size_sampled_rows(gpu):
     _ffn_case(gpu, p["M"], p["K"], p["F"], p["N"], p["seed"], rows=rows)
 
 
+@pytest.mark.parametrize("M,K,F,N,gated,gain", [
+    (256, 256, 320, 192, True, True),     # one M-tile; F % 128 = 64: a half-empty column tile
+    (300, 128, 512, 64, True, False),     # ragged M (two M-tiles), no subln gain
+    (129, 192, 448, 100, True, True),     # K % 128 = 64 tail, 3.5 column tiles
+    (200, 256, 384, 96, False, True),     # no gate: separate product and tail
+], ids=["one_tile_ragged_f", "ragged_m_nogain", "k_tail", "ungated"])
+def test_ffn_prefill_paths(gpu, M, K, F, N, gated, gain):
+    """M >= 128 with a gate runs the fused gate/up kernel and the partial-sum
+    tail; every row is compared with the oracle."""
+    _ffn_case(gpu, M, K, F, N, 80 + M, gated=gated, gain=gain)
+
+
+def test_ffn_prefill_zero_token_and_determinism(gpu):
+    M, K, F, N = 260, 128, 384, 64
+    Wg, Wu, Wd, X = workloads.ffn_problem(71, M, K, F, N)
+    Wgp, gg = _gpu_weight(gpu, Wg)
+    Wup, gu = _gpu_weight(gpu, Wu)
+    Wdp, gd = _gpu_weight(gpu, Wd)
+    X[5] = 0
+    X[259] = 0
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    out1 = gpu.bitlinear_ffn_relu2(Xq, d, Wgp, gg, Wup, gu, Wdp, gd, want_debug=True)
+    out2 = gpu.bitlinear_ffn_relu2(Xq, d, Wgp, gg, Wup, gu, Wdp, gd, want_debug=True)
+    torch.cuda.synchronize()
+    Y, Hq, dh = out1
+    for r in (5, 259):
+        assert dh[r].item() == 0 and not Hq[r].any() and not Y[r].any()
+    for a, b in zip(out1, out2):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.int8 else a.view(torch.int32),
+                           b.view(torch.uint8) if b.dtype == torch.int8 else b.view(torch.int32))
+
+
 def test_ffn_zero_token(gpu):
     """An all-zero token gives zero codes, dh = 0 and a zero output row."""
     M, K, F, N = 3, 128, 256, 64
