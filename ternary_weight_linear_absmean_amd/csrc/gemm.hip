@@ -124,6 +124,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 //   <2, 4, 2, 2>: 128 x 256 tiles, 512 threads (narrow N, e.g. K6912 -> N2560,
 //                 where 256 x 256 tiles would leave most CUs idle): measured
 //                 59 us on M2048 K6912 N2560 against 73 us for 128 x 128
+//                 tiles of 128 threads, with the same epilogue
+//   <2, 4, 4, 2> in gate/up mode (GU): the FFN's gate and up products in one
+//                 kernel, 256 x 128 outputs per tile (see GateUp below)
 // k-step 128: the activation tile (transposed 16-byte groups, see
 // device_common.h) and the packed weight tile (2-bit codes, 4x smaller than
 // int8) are staged in LDS, double-buffered, from registers loaded two
@@ -324,9 +327,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     const int b_off = (wn * 32 * NJ2 + (lane & 31)) * kBPitch + (lane >> 5);
     // The loads for k-step kt + 2 are issued on every step, past the end
     // from the last k-step again (a valid address, never stored to LDS):
-    // with no branch around them the compiler counts exactly five loads
-    // in flight behind the stage it stores, and waits for that stage only
-    // instead of draining everything issued this step.
+    // with no branch around them the compiler knows that exactly one
+    // stage's loads are in flight behind the stage it stores, and waits for
+    // that stage only instead of draining everything issued this step.
     // The row factors are read once, ahead of the operand loads, and kept in
     // LDS: the epilogue then issues no global load, so its stores never wait
     // behind one (the vector-memory counter retires loads and stores in order).

@@ -279,7 +279,8 @@ def test_ffn_prefill_full_size_sampled_rows(gpu):
     (300, 128, 512, 64, True, False),     # ragged M (two M-tiles), no subln gain
     (129, 192, 448, 100, True, True),     # K % 128 = 64 tail, 3.5 column tiles
     (200, 256, 384, 96, False, True),     # no gate: separate product and tail
-], ids=["one_tile_ragged_f", "ragged_m_nogain", "k_tail", "ungated"])
+    (128, 64, 256, 64, True, True),       # K = 64: no full k-step, the tail step only
+], ids=["one_tile_ragged_f", "ragged_m_nogain", "k_tail", "ungated", "k64"])
 def test_ffn_prefill_paths(gpu, M, K, F, N, gated, gain):
     """M >= 128 with a gate runs the fused gate/up kernel and the partial-sum
     tail; every row is compared with the oracle."""
