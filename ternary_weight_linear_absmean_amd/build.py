@@ -19,8 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 
-SOURCES = ["api.cpp", "quant.hip", "gemv.hip", "gemm.hip", "ffn.hip", "stack.hip",
-           "stack_persistent.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemv.hip", "gemm.hip", "gemm_skinny.hip", "ffn.hip",
+           "stack.hip", "stack_persistent.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

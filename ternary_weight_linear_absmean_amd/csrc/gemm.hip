@@ -482,6 +482,8 @@ hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *W
                        hipStream_t s) {
     if (M == 0 || N == 0)
         return hipSuccess;
+    if (M < 128 && gemm_skinny_fits(M, K))
+        return launch_gemm_skinny(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
     if (M >= 128) {
         int cfg = (N >= 4096 && M >= 256) ? 0 : 1;
 #ifdef BL_GEMM_CFG

@@ -30,6 +30,13 @@ hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *W
                        const float *gamma, int N, int K, float *Y, int32_t *acc,
                        hipStream_t s);
 
+// Few-token product on int8 MFMA that reads every packed weight once
+// (gemm_skinny.hip): 1 <= M < 128, 64 <= K <= 8192, K % 64 == 0.
+bool gemm_skinny_fits(int M, int K);
+hipError_t launch_gemm_skinny(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
+                              const float *gamma, int N, int K, float *Y, int32_t *acc,
+                              hipStream_t s);
+
 // Largest M the VALU kernel takes in one pass over the weights.
 constexpr int kGemvMaxTokens = 8;
 

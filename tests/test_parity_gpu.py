@@ -161,6 +161,22 @@ def test_gemv_ragged(gpu, M, K, N):
     _product_case(gpu, "bitlinear_gemv", M, K, N, 300 + N)
 
 
+@pytest.mark.parametrize("call,M,K,N", [
+    ("bitlinear_gemm", 1, 6912, 100),     # few-token kernel, codes resident in LDS
+    ("bitlinear_gemm", 9, 6912, 65),      # the largest resident case at K = 6912
+    ("bitlinear_gemm", 10, 6912, 65),     # chunked, one 32-token block
+    ("bitlinear_gemm", 33, 576, 97),      # two token blocks; last chunk 64 wide
+    ("bitlinear_gemm", 100, 8192, 40),    # four token blocks at the largest K it takes
+    ("bitlinear_gemm", 127, 64, 33),      # one partial chunk, ragged N
+    ("bitlinear_gemm", 5, 8256, 64),      # K past 8192: the 128 x 128 tile kernel
+    ("bitlinear_gemv", 3, 320, 641),      # v_dot4 hands over to the MFMA kernel at M = 3
+    ("bitlinear_gemv", 64, 8192, 50),
+    ("bitlinear_gemv", 40, 8256, 30),     # K past 8192: v_dot4 path
+], ids=lambda v: str(v))
+def test_few_token_kernel_paths(gpu, call, M, K, N):
+    _product_case(gpu, call, M, K, N, 500 + M + N)
+
+
 def test_tiny_config(gpu):
     t = workloads.TINY
     for call in ("bitlinear_gemv", "bitlinear_gemm"):
