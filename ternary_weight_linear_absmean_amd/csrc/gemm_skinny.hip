@@ -256,6 +256,129 @@ __global__ __launch_bounds__(kSkThreads) void gemm_skinny_res_kernel(
     }
 }
 
+// Narrow-N variant on v_mfma_i32_16x16x64_i8: 16 weight rows per workgroup,
+// so N = 2560 spreads over 160 workgroups instead of 80 (each CU streams half
+// as many bytes).  Chunks are 1024 wide and wave w takes the 256-wide quarter
+// w: lane (r = lane % 16, g = lane / 16) reads the 64 weights
+// [kq + 64 g, +64) of row r as one 16-byte unit and uses its dword t in
+// MFMA step t (k in [kq + 64 g + 16 t, +16) on lane group g, kq the quarter's
+// first k); the A operand of token m on lane group g is activation group
+// kq / 16 + 4 g + t.  Tokens come in MB blocks of 16.
+constexpr int kS16Chunk = 1024;
+constexpr int kS16MaxChunks = 8;                  // K <= 8192
+constexpr int kS16Pitch = kS16Chunk / 16 + 1;     // uint4 per staged token row (+1 pad)
+
+template <int MB>
+__device__ __forceinline__ void load_chunk16(uint4 (&a)[MB * 4], const int8_t *__restrict__ Xq,
+                                             int M, int K, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < MB * 4; ++i) {
+        const int e = tid + kSkThreads * i;                      // token e / 64, group e % 64
+        const int tk = e >> 6, k = k0 + 16 * (e & 63);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tk < M && k < K) v = *reinterpret_cast<const uint4 *>(Xq + (size_t)tk * K + k);
+        a[i] = v;
+    }
+}
+template <int MB>
+__device__ __forceinline__ void store_chunk16(const uint4 (&a)[MB * 4], uint4 *buf, int tid) {
+#pragma unroll
+    for (int i = 0; i < MB * 4; ++i) {
+        const int e = tid + kSkThreads * i;
+        buf[(e >> 6) * kS16Pitch + (e & 63)] = transpose16(a[i]);
+    }
+}
+
+template <int MB>
+__global__ __launch_bounds__(kSkThreads) void gemm_skinny16_kernel(
+    const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
+    const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
+    float *__restrict__ Y, int32_t *__restrict__ acc_out) {
+    constexpr int kStage = 16 * MB * kS16Pitch;
+    __shared__ uint4 As[2 * kStage];
+    __shared__ float cS[16 * MB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int nch = (K + kS16Chunk - 1) / kS16Chunk;
+    const int KB = K / 4;
+
+    const uint8_t *wrow = Wp + (size_t)min(n0 + (lane & 15), N - 1) * KB;
+    uint4 w[kS16MaxChunks];
+#pragma unroll
+    for (int c = 0; c < kS16MaxChunks; ++c) {
+        if (c < nch) {
+            const int off = 256 * c + 64 * wave + 16 * (lane >> 4);   // bytes: quarter + unit
+            const uint4 v = *reinterpret_cast<const uint4 *>(wrow + min(off, KB - 16));
+            w[c] = off < KB ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    constexpr int PF = MB <= 2 ? 2 : 1;
+    const float g = scalar_load(gamma);
+    if (tid < 16 * MB) cS[tid] = tid < M ? __fmul_rn(g, d[tid]) : 0.0f;
+    uint4 a[PF][MB * 4];
+    load_chunk16<MB>(a[0], Xq, M, K, 0, tid);
+    if constexpr (PF == 2) {
+        if (nch > 1) load_chunk16<MB>(a[1], Xq, M, K, kS16Chunk, tid);
+    }
+    store_chunk16<MB>(a[0], As, tid);
+    if (nch > PF) load_chunk16<MB>(a[0], Xq, M, K, PF * kS16Chunk, tid);
+    __syncthreads();
+
+    v4i acc[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[b] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < kS16MaxChunks; ++c) {
+        if (c < nch) {
+            const uint4 *A = As + (c & 1) * kStage;
+            const uint32_t dws[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                uint4 bv;
+                unpack16(dws[t], bv.x, bv.y, bv.z, bv.w);
+                const v4i bf = as_v4i(bv);
+                const int grp = 16 * wave + 4 * (lane >> 4) + t;
+#pragma unroll
+                for (int b = 0; b < MB; ++b) {
+                    const v4i af = as_v4i(A[(16 * b + (lane & 15)) * kS16Pitch + grp]);
+                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[b], 0, 0, 0);
+                }
+            }
+            if (c + 1 < nch) {
+                store_chunk16<MB>(a[(c + 1) % PF], As + ((c + 1) & 1) * kStage, tid);
+                if (c + 1 + PF < nch)
+                    load_chunk16<MB>(a[(c + 1) % PF], Xq, M, K, (c + 1 + PF) * kS16Chunk, tid);
+            }
+            __syncthreads();
+        }
+    }
+
+    // the four waves' sums: [4][MB][4][64] through LDS, then 16 x M outputs
+    int *red = reinterpret_cast<int *>(As);
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[((wave * MB + b) * 4 + r) * 64 + lane] = acc[b][r];
+    __syncthreads();
+    if (tid < MB * 64) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int b = tid >> 6, l = tid & 63;
+            int sum = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sum += red[((v * MB + b) * 4 + r) * 64 + l];
+            const int lt = 16 * b + 4 * (l >> 4) + r;            // token
+            const int col = n0 + (l & 15);
+            if (lt < M && col < N) {
+                const size_t o = (size_t)lt * N + col;
+                Y[o] = rescale(sum, cS[lt]);
+                if (acc_out) acc_out[o] = sum;
+            }
+        }
+    }
+}
+
 // The resident layout holds M rows of K / 16 + 1 groups, and the last chunk
 // may read up to 31 groups past a row's end: M (K / 16 + 1) + 32 <= 4096.
 bool res_fits(int M, int K) { return M <= 32 && M * (K / 16 + 1) + 32 <= kResGroups; }
@@ -271,6 +394,20 @@ hipError_t launch_gemm_skinny(const int8_t *Xq, const float *d, int M, const uin
                               hipStream_t s) {
     if (M == 0 || N == 0)
         return hipSuccess;
+    // Narrow N: 16-row workgroups when 32-row ones would leave most CUs idle.
+    if (N <= 4096 && M <= 64) {
+        const dim3 grid16((N + 15) / 16);
+        if (M <= 16)
+            hipLaunchKernelGGL(gemm_skinny16_kernel<1>, grid16, dim3(kSkThreads), 0, s, Xq, d, M, Wp,
+                               gamma, N, K, Y, acc);
+        else if (M <= 32)
+            hipLaunchKernelGGL(gemm_skinny16_kernel<2>, grid16, dim3(kSkThreads), 0, s, Xq, d, M, Wp,
+                               gamma, N, K, Y, acc);
+        else
+            hipLaunchKernelGGL(gemm_skinny16_kernel<4>, grid16, dim3(kSkThreads), 0, s, Xq, d, M, Wp,
+                               gamma, N, K, Y, acc);
+        return hipGetLastError();
+    }
     const dim3 grid((N + 31) / 32);
     if (res_fits(M, K))
         hipLaunchKernelGGL(gemm_skinny_res_kernel, grid, dim3(kSkThreads), 0, s, Xq, d, M, Wp, gamma,

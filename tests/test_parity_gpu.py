@@ -162,16 +162,22 @@ def test_gemv_ragged(gpu, M, K, N):
 
 
 @pytest.mark.parametrize("call,M,K,N", [
-    ("bitlinear_gemm", 1, 6912, 100),     # few-token kernel, codes resident in LDS
-    ("bitlinear_gemm", 9, 6912, 65),      # the largest resident case at K = 6912
-    ("bitlinear_gemm", 10, 6912, 65),     # chunked, one 32-token block
-    ("bitlinear_gemm", 33, 576, 97),      # two token blocks; last chunk 64 wide
-    ("bitlinear_gemm", 100, 8192, 40),    # four token blocks at the largest K it takes
+    # N <= 4096, M <= 64: 16-row workgroups (16x16x64), token blocks of 16
+    ("bitlinear_gemm", 1, 6912, 100),     # one block, 7 chunks (the last 768 wide)
+    ("bitlinear_gemm", 17, 6912, 65),     # two blocks
+    ("bitlinear_gemm", 33, 576, 97),      # four blocks; one chunk of 576
+    ("bitlinear_gemv", 3, 320, 641),      # v_dot4 hands over to the MFMA kernels at M = 3
+    ("bitlinear_gemv", 64, 8192, 50),     # the largest K the few-token kernels take
+    # wider N, or M > 64: 32-row workgroups (32x32x32), token blocks of 32
+    ("bitlinear_gemm", 8, 6912, 4160),    # codes resident in LDS (M * K <= 64 KB)
+    ("bitlinear_gemm", 9, 6912, 4110),    # the largest resident case at K = 6912
+    ("bitlinear_gemm", 20, 2560, 4200),   # chunked, one block, chunks two ahead
+    ("bitlinear_gemm", 40, 576, 4200),    # two blocks; last chunk 64 wide
+    ("bitlinear_gemm", 100, 8192, 40),    # four blocks (M > 64), one chunk ahead
     ("bitlinear_gemm", 127, 64, 33),      # one partial chunk, ragged N
-    ("bitlinear_gemm", 5, 8256, 64),      # K past 8192: the 128 x 128 tile kernel
-    ("bitlinear_gemv", 3, 320, 641),      # v_dot4 hands over to the MFMA kernel at M = 3
-    ("bitlinear_gemv", 64, 8192, 50),
-    ("bitlinear_gemv", 40, 8256, 30),     # K past 8192: v_dot4 path
+    # K past 8192: the earlier paths
+    ("bitlinear_gemm", 5, 8256, 64),      # the 128 x 128 tile kernel
+    ("bitlinear_gemv", 40, 8256, 30),     # v_dot4
 ], ids=lambda v: str(v))
 def test_few_token_kernel_paths(gpu, call, M, K, N):
     _product_case(gpu, call, M, K, N, 500 + M + N)
