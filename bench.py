@@ -13,7 +13,9 @@ B for the four shapes) over the
 measured step time, in GB/s.  The same step as separate quant + GEMV calls
 is reported as ``decode_unfused``.
 
-Also measured in the same run and reported beside it: the prefill GEMM
+Also measured in the same run and reported beside it: batched decode
+(bitlinear_gemv on M = 8 / 32 / 64 tokens, K2560->N6912 and K6912->N2560,
+cold weights, per launch), the prefill GEMM
 (M = 2048, K2560->N6912, int8 TOPS against the int8 MFMA peak), the prefill
 FFN tail (gate/up, ReLU² + subln + requant, down), one decode token through
 the full 30-layer linear stack (bitlinear_decode_stack: 521 MB of packed
@@ -75,7 +77,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--part", default="all", choices=["all", "decode", "gemm", "ffn", "stack", "copy"],
+    ap.add_argument("--part", default="all",
+                    choices=["all", "decode", "batched", "gemm", "ffn", "stack", "copy"],
                     help="restrict the GPU legs (for profiling runs); 'copy' (not in 'all') "
                          "times a plain device copy of 256 MiB, the reference for the "
                          "byte counters")
@@ -319,6 +322,38 @@ def bench_stack(bl, torch, workloads, steps, warmup):
                                    launches_per_token=2 + 8 * L))
 
 
+def bench_batched(bl, torch, workloads):
+    """Batched decode: bitlinear_gemv on M in {8, 32, 64} pre-quantised
+    tokens against K2560->N6912 and K6912->N2560, weights rotated over
+    copies past the Infinity Cache, launches replayed from HIP graphs; the
+    time per launch includes the dispatch gap."""
+    shapes = workloads.BATCHED_SHAPES
+    reps = STEPS_PER_GRAPH * math.ceil(max(2, math.ceil(COLD_BYTES / min(
+        s.N * s.K // 4 for s in shapes))) / STEPS_PER_GRAPH)
+    rows = []
+    for i, s in enumerate(shapes):
+        W, _ = workloads.bitlinear_problem(70 + i, 1, s.K, s.N)
+        Wp, g = bl.quant_weight_absmean_pack(W.cuda())
+        copies = [Wp] + [Wp.clone() for _ in range(reps - 1)]
+        for M in workloads.BATCHED_M:
+            _, X = workloads.bitlinear_problem(80 + M, M, s.K, 1)
+            Xq, d = bl.quant_act_absmax_i8(X.cuda())
+            Y = torch.empty((M, s.N), dtype=torch.float32, device="cuda")
+
+            def step(r):
+                bl.bitlinear_gemv(Xq, d, copies[r], g, Y=Y)
+            for r in range(reps):
+                step(r)
+            torch.cuda.synchronize()
+            graphs = capture(torch, step, reps, STEPS_PER_GRAPH)
+            ms = replay_ms(torch, graphs, 2 * reps, STEPS_PER_GRAPH, STEPS_PER_GRAPH)
+            us = 1000.0 * ms / (2 * reps)
+            nbytes = s.N * s.K // 4 + M * s.K + 4 * M * s.N + 4 * M + 4
+            rows.append(dict(M=M, K=s.K, N=s.N, us=round(us, 2), GBs=round(nbytes / us / 1e3, 1)))
+        del copies
+    return rows
+
+
 def bench_copy(torch, steps):
     """A plain device-to-device copy of 256 MiB: the kernel whose HBM byte
     counters (FETCH_SIZE, WRITE_SIZE) calibrate the ones read for the GEMV."""
@@ -398,6 +433,8 @@ def main():
         out["decode_unfused"] = dec["unfused"]
         out["config"]["weight_copies"] = dec["reps"]
         out["config"]["step_bytes"] = dec["step_bytes"]
+    if args.part in ("all", "batched"):
+        out["batched_decode"] = bench_batched(bl, torch, workloads)
     if args.part in ("all", "gemm"):
         out["gemm"] = bench_gemm(bl, torch, workloads, max(10, args.steps // 8), 5)
     if args.part in ("all", "ffn"):
