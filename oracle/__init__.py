@@ -245,3 +245,25 @@ def decode_stack(x0, layers, H, KV, F, D, eps):
         x = np.add(x_mid, y, dtype=np.float32)
     trace = np.stack(rows) if rows else np.zeros((0, 5 * H + 2 * KV), np.float32)
     return x, trace
+
+
+# ------------------------------------------------------------------ QAT backward
+# "Microsoft BitNet 深度研究报告", §2 (4) 量化感知训练: the forward uses the
+# quantised weights, the backward passes the gradient through the quantisers
+# with the straight-through estimator, and the optimiser updates the original
+# (latent) weights.  Reading taken: the forward is Y = X~ W~^T with
+# X~ = Xq * d (per-token absmax) and W~ = gamma * Wq (absmean); the STE treats
+# both quantisers as the identity, so the gradients of the latent X and W are
+# those of the linear map at X~, W~.  Plain fp64; numpy matmul is the
+# contraction.
+
+def backward_input(dY, Wp, gamma, K):
+    """dX = dY . W~, W~ = gamma * Wq: fp64 [M, K] from dY [M, N]."""
+    Wq = unpack(Wp, K).astype(np.float64)                     # [N, K] in {-1, 0, 1}
+    return (np.asarray(dY, dtype=np.float64) @ Wq) * float(np.float32(gamma))
+
+
+def backward_weight(dY, Xq, d):
+    """dW = dY^T . X~, X~ = Xq * d (row m scaled by d[m]): fp64 [N, K]."""
+    G = np.asarray(dY, dtype=np.float64) * np.asarray(d, dtype=np.float64)[:, None]
+    return G.T @ np.asarray(Xq, dtype=np.float64)
