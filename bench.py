@@ -19,8 +19,9 @@ cold weights, per launch), the prefill GEMM
 (M = 2048, K2560->N6912, int8 TOPS against the int8 MFMA peak), the prefill
 FFN tail (gate/up, ReLU² + subln + requant, down), one decode token through
 the full 30-layer linear stack (bitlinear_decode_stack: 521 MB of packed
-weights per token, tokens/s and GB/s) and the CPU oracle on a bounded sample
-of the decode step.
+weights per token, tokens/s and GB/s), the QAT backward (dX and dW at
+M = 2048 for the FFN shapes) and the CPU oracle on a bounded sample of the
+decode step.
 
 Prints one JSON line.
 """
@@ -38,6 +39,7 @@ if ROOT not in sys.path:
 METRIC = "BitLinear M=1 GEMV GB/s (% HBM peak); M=2048 GEMM int8 TOPS (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 I8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 COLD_BYTES = 600 * 2 ** 20     # > 2 x 256 MB Infinity Cache
 
 
@@ -78,7 +80,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--part", default="all",
-                    choices=["all", "decode", "batched", "gemm", "ffn", "stack", "copy"],
+                    choices=["all", "decode", "batched", "gemm", "ffn", "stack", "qat", "copy"],
                     help="restrict the GPU legs (for profiling runs); 'copy' (not in 'all') "
                          "times a plain device copy of 256 MiB, the reference for the "
                          "byte counters")
@@ -245,6 +247,45 @@ def bench_ffn(bl, torch, workloads, steps, warmup):
     us = 1000.0 * t0.elapsed_time(t1) / steps
     ops = 2.0 * M * K * F * 2 + 2.0 * M * F * N
     return dict(M=M, K=K, F=F, N=N, us=round(us, 2), TOPS=round(ops / us / 1e6, 1))
+
+
+def bench_qat(bl, torch, workloads, steps, warmup):
+    """QAT backward at M = 2048 tokens for the FFN shapes: dX and dW, each
+    timed over back-to-back calls (transposes + product) between two events.
+    TFLOPs counts the 2 M N K algorithmic flops of each gradient; the bf16
+    MFMA issues twice that (the hi and lo halves of the fp32 gradient)."""
+    out = []
+    for sh in workloads.QAT_SHAPES:
+        M, K, N = workloads.QAT_M, sh.K, sh.N
+        W, X, dY = workloads.qat_problem(600 + K, M, K, N)
+        Wp, g = bl.quant_weight_absmean_pack(W.cuda())
+        Xq, d = bl.quant_act_absmax_i8(X.cuda())
+        dY = dY.cuda()
+        dX = torch.empty((M, K), dtype=torch.float32, device="cuda")
+        dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        wsi = torch.empty((bl.workspace_bytes(bl.BL_OP_BACKWARD_INPUT, M, N, K),),
+                          dtype=torch.uint8, device="cuda")
+        wsw = torch.empty((bl.workspace_bytes(bl.BL_OP_BACKWARD_WEIGHT, M, N, K),),
+                          dtype=torch.uint8, device="cuda")
+        row = dict(M=M, K=K, N=N)
+        for name, fn in (("dX", lambda: bl.bitlinear_backward_input(dY, Wp, g, dX=dX, ws=wsi)),
+                         ("dW", lambda: bl.bitlinear_backward_weight(dY, Xq, d, dW=dW, ws=wsw))):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            us = 1000.0 * t0.elapsed_time(t1) / steps
+            tf = 2.0 * M * N * K / us / 1e6
+            row[name] = dict(us=round(us, 2), TFLOPs=round(tf, 1),
+                             mfma_frac_bf16=round(2.0 * tf / BF16_MFMA_PEAK_TFLOPS, 4))
+        out.append(row)
+    return out
 
 
 STACK_SEED = 4242
@@ -439,6 +480,8 @@ def main():
         out["gemm"] = bench_gemm(bl, torch, workloads, max(10, args.steps // 8), 5)
     if args.part in ("all", "ffn"):
         out["ffn"] = bench_ffn(bl, torch, workloads, max(5, args.steps // 40), 2)
+    if args.part in ("all", "qat"):
+        out["qat_backward"] = bench_qat(bl, torch, workloads, max(5, args.steps // 40), 2)
     if args.part == "copy":
         out["copy"] = bench_copy(torch, 10)
     if args.part in ("all", "stack"):

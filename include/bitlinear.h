@@ -87,7 +87,9 @@ typedef enum {
 typedef enum {
     BL_OP_QUANT_WEIGHT = 0,   /* quant_weight_absmean_pack */
     BL_OP_FFN_RELU2 = 1,      /* bitlinear_ffn_relu2 */
-    BL_OP_DECODE_STACK = 2    /* bitlinear_decode_stack: N = H, K = KV, F = F */
+    BL_OP_DECODE_STACK = 2,   /* bitlinear_decode_stack: N = H, K = KV, F = F */
+    BL_OP_BACKWARD_INPUT = 3, /* bitlinear_backward_input */
+    BL_OP_BACKWARD_WEIGHT = 4 /* bitlinear_backward_weight */
 } bl_op;
 
 /* Largest K (and F) any call accepts: keeps |acc| <= 127 K exact in int32
@@ -289,6 +291,52 @@ enum { BL_STACK_AUTO = 0, BL_STACK_LAUNCHES = 1, BL_STACK_PERSISTENT = 2 };
 bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers, const bl_stack_dims *dims,
                                  float *x, float *trace, void *ws, size_t ws_bytes,
                                  void *stream);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_backward_input / bitlinear_backward_weight -- the backward pass
+ * of quantisation-aware training through one BitLinear.
+ * [RPT] §2 (4) 量化感知训练: the forward uses the quantised weights, the
+ * backward goes through the quantisers with the straight-through estimator,
+ * and the optimiser updates the latent weights.  With the forward operands
+ * X~ = Xq d (per token) and W~ = gamma Wq, the straight-through gradients of
+ * the latent X and W are
+ *     dX = dY . W~  = gamma (dY . Wq)          fp32 [M][K]
+ *     dW = dY^T . X~ = (dY o d)^T . Xq         fp32 [N][K]
+ * The integer operands are exact in bf16; each fp32 gradient value is split
+ * into two bf16 halves (hi + lo, to about 2^-17 of the value) and both run on
+ * bf16 MFMA with fp32 accumulation.  Each result element is within
+ * 1e-3 * sum_c |term_c| of the exact sum (the terms being the products it
+ * adds).  Gradients must be finite and below 2^127 in magnitude.
+ * An empty sum (N == 0 for dX, M == 0 for dW) writes zeros and reads no
+ * operand (those pointers may then be NULL); an empty output is a no-op.
+ * Both are asynchronous on `stream`; errors as for bitlinear_gemm.
+ *
+ * bitlinear_backward_input:
+ *   dY     in   fp32 [M][N], 16-byte aligned; N % 4 == 0.
+ *   Wp     in   uint8 [N][K/4], 16-byte aligned: the forward's packed weights.
+ *   gamma  in   fp32 [1], the forward's weight scale.
+ *   M, N, K     0 <= M, N < 2^31 - 63; K % 64 == 0; K <= BL_MAX_K.
+ *   dX     out  fp32 [M][K].
+ *   ws          >= bl_workspace_bytes(BL_OP_BACKWARD_INPUT, M, N, K, 0) bytes,
+ *               16-byte aligned (the weights unpacked to int8, transposed).
+ * bitlinear_backward_weight:
+ *   dY     in   fp32 [M][N], 16-byte aligned.
+ *   Xq     in   int8 [M][K], 16-byte aligned;  d  in  fp32 [M]: the forward's
+ *               quantised input (quant_act_absmax_i8).
+ *   M, N, K     as above (N any).
+ *   dW     out  fp32 [N][K].
+ *   ws          >= bl_workspace_bytes(BL_OP_BACKWARD_WEIGHT, M, N, K, 0) bytes,
+ *               16-byte aligned ((dY o d)^T in fp32 and Xq^T).
+ * The forward of a training step is quant_weight_absmean_pack on the latent
+ * weights, quant_act_absmax_i8 and bitlinear_gemm; the optimiser step is the
+ * caller's.
+ */
+bl_status bitlinear_backward_input(const float *dY, int64_t M, int64_t N, const uint8_t *Wp,
+                                   const float *gamma, int64_t K, float *dX, void *ws,
+                                   size_t ws_bytes, void *stream);
+bl_status bitlinear_backward_weight(const float *dY, int64_t M, int64_t N, const int8_t *Xq,
+                                    const float *d, int64_t K, float *dW, void *ws,
+                                    size_t ws_bytes, void *stream);
 
 /* Workspace bytes a call needs for the given sizes (0 for calls that need
  * none; arguments a call does not use are ignored). */

@@ -5,9 +5,10 @@ Importing the package does not load the native library; the first call (or
 ``load()``) does, and raises if it has not been built.
 """
 from ._native import (  # noqa: F401
-    BL_BF16, BL_F32, BL_MAX_JOBS, BL_MAX_K, BL_OP_DECODE_STACK, BL_OP_FFN_RELU2,
-    BL_OP_QUANT_WEIGHT, BL_STACK_AUTO, BL_STACK_LAUNCHES, BL_STACK_PERSISTENT, EXPORTS, LAYER_GAMMAS, LAYER_WEIGHTS, LIB_PATH, BitLinearError,
-    GemvJob, Layer, StackDims, bitlinear_decode_stack, bitlinear_ffn_relu2, bitlinear_gemm,
-    bitlinear_gemv, bitlinear_gemv_fused, load,
-    quant_act_absmax_i8, quant_weight_absmean_pack, workspace_bytes,
+    BL_BF16, BL_F32, BL_MAX_JOBS, BL_MAX_K, BL_OP_BACKWARD_INPUT, BL_OP_BACKWARD_WEIGHT,
+    BL_OP_DECODE_STACK, BL_OP_FFN_RELU2, BL_OP_QUANT_WEIGHT, BL_STACK_AUTO, BL_STACK_LAUNCHES,
+    BL_STACK_PERSISTENT, EXPORTS, LAYER_GAMMAS, LAYER_WEIGHTS, LIB_PATH, BitLinearError,
+    GemvJob, Layer, StackDims, bitlinear_backward_input, bitlinear_backward_weight,
+    bitlinear_decode_stack, bitlinear_ffn_relu2, bitlinear_gemm, bitlinear_gemv,
+    bitlinear_gemv_fused, load, quant_act_absmax_i8, quant_weight_absmean_pack, workspace_bytes,
 )

@@ -26,9 +26,11 @@ STATUS = {0: "BL_OK", 1: "BL_ERR_NULL", 2: "BL_ERR_SHAPE", 3: "BL_ERR_DTYPE",
 
 EXPORTS = ["quant_weight_absmean_pack", "quant_act_absmax_i8", "bitlinear_gemv",
            "bitlinear_gemm", "bitlinear_gemv_fused", "bitlinear_ffn_relu2",
-           "bitlinear_decode_stack", "bl_workspace_bytes", "bl_status_string",
-           "bl_last_error", "bl_abi_version"]
+           "bitlinear_decode_stack", "bitlinear_backward_input", "bitlinear_backward_weight",
+           "bl_workspace_bytes", "bl_status_string", "bl_last_error", "bl_abi_version"]
 BL_OP_DECODE_STACK = 2
+BL_OP_BACKWARD_INPUT = 3
+BL_OP_BACKWARD_WEIGHT = 4
 LAYER_WEIGHTS = ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd")
 LAYER_GAMMAS = ("gq", "gk", "gv", "go", "gg", "gu", "gd")
 
@@ -96,6 +98,10 @@ def load():
     lib.bitlinear_ffn_relu2.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p,
                                         ctypes.c_float, _p, _p, _i64, _p, _p, _p, _p, _sz, _p]
     lib.bl_workspace_bytes.restype = _sz
+    for name in ("bitlinear_backward_input", "bitlinear_backward_weight"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [_p, _i64, _i64, _p, _p, _i64, _p, _p, _sz, _p]
     lib.bl_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64]
     lib.bl_status_string.restype = ctypes.c_char_p
     lib.bl_status_string.argtypes = [ctypes.c_int]
@@ -317,3 +323,47 @@ def bitlinear_decode_stack(layers, x, H, KV, F, D, eps=1e-5, trace=False, ws=Non
     _check("bitlinear_decode_stack", load().bitlinear_decode_stack(
         arr, n, ctypes.byref(dims), _ptr(x), _ptr(tr), _ptr(ws), ws.numel(), _stream(stream)))
     return tr
+
+
+def bitlinear_backward_input(dY, Wp, gamma, dX=None, ws=None, stream=None):
+    """Straight-through gradient of the layer input: dX [M, K] = gamma (dY . Wq)
+    for dY fp32 [M, N] and the forward's packed Wp [N, K/4], gamma [1]."""
+    _dev(dY, torch.float32, "dY")
+    _dev(Wp, torch.uint8, "Wp")
+    _dev(gamma, torch.float32, "gamma")
+    M, N = dY.shape
+    if Wp.dim() != 2 or Wp.shape[0] != N:
+        raise ValueError(f"Wp must be [N, K/4] with N = {N}, got {tuple(Wp.shape)}")
+    K = Wp.shape[1] * 4
+    dX = _dev(dX, torch.float32, "dX") if dX is not None else torch.empty(
+        (M, K), dtype=torch.float32, device=dY.device)
+    if tuple(dX.shape) != (M, K):
+        raise ValueError(f"dX must be [{M}, {K}]")
+    need = workspace_bytes(BL_OP_BACKWARD_INPUT, M, N, K, 0)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dY.device)
+    _check("bitlinear_backward_input", load().bitlinear_backward_input(
+        _ptr(dY), M, N, _ptr(Wp), _ptr(gamma), K, _ptr(dX), _ptr(ws), ws.numel(), _stream(stream)))
+    return dX
+
+
+def bitlinear_backward_weight(dY, Xq, d, dW=None, ws=None, stream=None):
+    """Straight-through gradient of the latent weights: dW [N, K] =
+    (dY o d)^T . Xq for dY fp32 [M, N] and the forward's Xq int8 [M, K], d [M]."""
+    _dev(dY, torch.float32, "dY")
+    _dev(Xq, torch.int8, "Xq")
+    _dev(d, torch.float32, "d")
+    M, N = dY.shape
+    if Xq.dim() != 2 or Xq.shape[0] != M or tuple(d.shape) != (M,):
+        raise ValueError(f"Xq must be [{M}, K] and d [{M}]")
+    K = Xq.shape[1]
+    dW = _dev(dW, torch.float32, "dW") if dW is not None else torch.empty(
+        (N, K), dtype=torch.float32, device=dY.device)
+    if tuple(dW.shape) != (N, K):
+        raise ValueError(f"dW must be [{N}, {K}]")
+    need = workspace_bytes(BL_OP_BACKWARD_WEIGHT, M, N, K, 0)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dY.device)
+    _check("bitlinear_backward_weight", load().bitlinear_backward_weight(
+        _ptr(dY), M, N, _ptr(Xq), _ptr(d), K, _ptr(dW), _ptr(ws), ws.numel(), _stream(stream)))
+    return dW

@@ -71,6 +71,7 @@ bl_status launched(hipError_t e, const char *what) {
 }
 
 constexpr int64_t kI32Max = 2147483647;
+constexpr int64_t kBackwardMax = kI32Max - 63;     // row lengths padded to 64 stay in int
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -155,6 +156,12 @@ BL_EXPORT size_t bl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int
     case BL_OP_DECODE_STACK:
         if (N < 0 || K < 0 || F < 0 || N > 16384 || K > 16384 || F > 16384) return 0;
         return round_up(bl::stack_ws_floats((int)N, (int)K, (int)F) * sizeof(float), 256);
+    case BL_OP_BACKWARD_INPUT:
+        if (K < 0 || N < 0 || N > kBackwardMax) return 0;
+        return round_up(bl::backward_input_ws_bytes(N, K), 256);
+    case BL_OP_BACKWARD_WEIGHT:
+        if (K < 0 || M < 0 || N < 0 || M > kBackwardMax) return 0;
+        return round_up(bl::backward_weight_ws_bytes(M, N, K), 256);
     default: return 0;
     }
 }
@@ -238,6 +245,70 @@ BL_EXPORT bl_status bitlinear_gemm(const int8_t *Xq, const float *d, int64_t M, 
     return launched(bl::launch_gemm(Xq, d, (int)M, Wp, gamma, (int)N, (int)K, Y, acc,
                                     static_cast<hipStream_t>(stream)),
                     "bitlinear_gemm");
+}
+
+// Shared checks of the two backward calls; *noop is set when the output has
+// no elements.  An empty contraction (N == 0 for dX, M == 0 for dW) still
+// runs, with no operand read: the product kernel writes the zeros.
+static bl_status check_backward(const char *name, const float *dY, int64_t M, int64_t N, int64_t K,
+                                const void *w, const float *scale, float *out, void *ws,
+                                size_t ws_bytes, size_t need, bool out_empty, bool sum_empty,
+                                bool *noop) {
+    *noop = false;
+    if (M < 0 || N < 0 || K < 0 || M > kBackwardMax || N > kBackwardMax)
+        return fail(BL_ERR_SHAPE, "%s: negative or too large size (M=%lld N=%lld K=%lld)", name,
+                    (long long)M, (long long)N, (long long)K);
+    if (K % 64 != 0 || K > BL_MAX_K)
+        return fail(BL_ERR_SHAPE, "%s: K=%lld must be a multiple of 64 and <= %d", name,
+                    (long long)K, BL_MAX_K);
+    if (out_empty) {
+        *noop = true;
+        return ok();
+    }
+    if (!out || (!sum_empty && (!dY || !w || !scale)))
+        return fail(BL_ERR_NULL, "%s: NULL pointer", name);
+    if (!sum_empty && (!aligned(dY, 16) || !aligned(w, 16)))
+        return fail(BL_ERR_ALIGN, "%s: dY and the integer operand must be 16-byte aligned", name);
+    if ((!sum_empty && !aligned(scale, 4)) || !aligned(out, 4))
+        return fail(BL_ERR_ALIGN, "%s: the scale and the output must be 4-byte aligned", name);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(BL_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", name, ws_bytes, ws,
+                    need);
+    if (!aligned(ws, 16))
+        return fail(BL_ERR_ALIGN, "%s: ws must be 16-byte aligned", name);
+    return check_arch();
+}
+
+BL_EXPORT bl_status bitlinear_backward_input(const float *dY, int64_t M, int64_t N, const uint8_t *Wp,
+                                             const float *gamma, int64_t K, float *dX, void *ws,
+                                             size_t ws_bytes, void *stream) {
+    const char *name = "bitlinear_backward_input";
+    if (N % 4 != 0)
+        return fail(BL_ERR_SHAPE, "%s: N=%lld must be a multiple of 4", name, (long long)N);
+    bool noop = false;
+    const size_t need = bl_workspace_bytes(BL_OP_BACKWARD_INPUT, M, N, K, 0);
+    bl_status st = check_backward(name, dY, M, N, K, Wp, gamma, dX, ws, ws_bytes, need,
+                                  M == 0 || K == 0, N == 0, &noop);
+    if (st != BL_OK || noop)
+        return st;
+    return launched(bl::launch_backward_input(dY, (int)M, (int)N, Wp, gamma, (int)K, dX, ws,
+                                              static_cast<hipStream_t>(stream)),
+                    name);
+}
+
+BL_EXPORT bl_status bitlinear_backward_weight(const float *dY, int64_t M, int64_t N, const int8_t *Xq,
+                                              const float *d, int64_t K, float *dW, void *ws,
+                                              size_t ws_bytes, void *stream) {
+    const char *name = "bitlinear_backward_weight";
+    bool noop = false;
+    const size_t need = bl_workspace_bytes(BL_OP_BACKWARD_WEIGHT, M, N, K, 0);
+    bl_status st = check_backward(name, dY, M, N, K, Xq, d, dW, ws, ws_bytes, need,
+                                  N == 0 || K == 0, M == 0, &noop);
+    if (st != BL_OK || noop)
+        return st;
+    return launched(bl::launch_backward_weight(dY, (int)M, (int)N, Xq, d, (int)K, dW, ws,
+                                               static_cast<hipStream_t>(stream)),
+                    name);
 }
 
 BL_EXPORT bl_status bitlinear_gemv_fused(const bl_gemv_job *jobs, int count, int64_t M,

@@ -220,3 +220,34 @@ def test_stack_validation(lib):
     assert call(wsb=need - 1) == WS
     assert call(ws=None) == WS
     assert call(ws=A4) == ALIGN
+
+
+def test_backward_validation(lib):
+    big = 1 << 40
+    fi, fw = lib.bitlinear_backward_input, lib.bitlinear_backward_weight
+    # workspace: Wq^T int8 with rows padded to 64; (dY o d)^T fp32 + Xq^T int8
+    assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_INPUT, 8, 2560, 6912, 0) == 6912 * 2560
+    assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_INPUT, 8, 100, 128, 0) == 128 * 128
+    assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_WEIGHT, 100, 6, 128, 0) == \
+        (6 * 128 * 4 + 255) // 256 * 256 + 128 * 128
+    for f in (fi, fw):
+        assert f(A16, -1, 8, A16, A4, 64, A4, A16, big, None) == SHAPE
+        assert f(A16, 2, 8, A16, A4, 96, A4, A16, big, None) == SHAPE           # K % 64
+        assert f(A16, 2, 8, A16, A4, 2 * bl.BL_MAX_K, A4, A16, big, None) == SHAPE
+        assert f(A16, 2 ** 31 - 1, 8, A16, A4, 64, A4, A16, big, None) == SHAPE
+        assert f(None, 2, 8, A16, A4, 64, A4, A16, big, None) == NULL
+        assert f(A16, 2, 8, None, A4, 64, A4, A16, big, None) == NULL
+        assert f(A16, 2, 8, A16, None, 64, A4, A16, big, None) == NULL
+        assert f(A16, 2, 8, A16, A4, 64, None, A16, big, None) == NULL
+        assert f(A4, 2, 8, A16, A4, 64, A4, A16, big, None) == ALIGN
+        assert f(A16, 2, 8, A4, A4, 64, A4, A16, big, None) == ALIGN
+        assert f(A16, 2, 8, A16, A1, 64, A4, A16, big, None) == ALIGN
+        assert f(A16, 2, 8, A16, A4, 64, A1, A16, big, None) == ALIGN
+        assert f(A16, 2, 8, A16, A4, 64, A4, A16, 16, None) == WS
+        assert f(A16, 2, 8, A16, A4, 64, A4, None, big, None) == WS
+        assert f(A16, 2, 8, A16, A4, 64, A4, A4, big, None) == ALIGN
+        assert f(None, 0, 0, None, None, 0, None, None, 0, None) == OK
+    assert fi(A16, 2, 6, A16, A4, 64, A4, A16, big, None) == SHAPE             # N % 4
+    # empty outputs are no-ops, even with NULL pointers
+    assert fi(None, 0, 8, None, None, 64, None, None, 0, None) == OK
+    assert fw(None, 3, 0, None, None, 64, None, None, 0, None) == OK

@@ -81,7 +81,9 @@ def test_quant_weight_golden_and_ties(gpu):
     s = torch.randint(0, 2, (96, 128), generator=workloads.generator(8)).float() * 2 - 1
     Wp, g = _gpu_weight(gpu, s * 0.0173)
     assert g.item() == np.float32(0.0173)
-    assert np.array_equal(oracle.unpack(Wp.cpu().numpy(), 128), s.numpy().astype(np.int8))
+    Wp_ref, g_ref = oracle.quantize_weight((s * 0.0173).numpy())
+    assert np.array_equal(oracle.unpack(Wp_ref, 128), s.numpy().astype(np.int8))
+    assert np.array_equal(Wp.cpu().numpy(), Wp_ref) and g.item() == g_ref
 
 
 def test_quant_weight_empty(gpu):
@@ -264,11 +266,16 @@ def _ffn_case(gpu, M, K, F, N, seed, gated=True, gain=True, eps=1e-5, rows=None)
                                         want_debug=True)
     torch.cuda.synchronize()
     Xq_ref, d_ref = _ref_act(X)
+    ref_w = {}
+    for name, W, Wp_gpu, g_gpu in (("g", Wg, Wgp, gg), ("u", Wu, Wup, gu), ("d", Wd, Wdp, gd)):
+        Wp_ref, g_ref = oracle.quantize_weight(W.numpy())
+        assert np.array_equal(Wp_gpu.cpu().numpy(), Wp_ref) and g_gpu.item() == g_ref
+        ref_w[name] = (Wp_ref, g_ref)
     if rows is None:
         rows = np.arange(M)
-    ref = oracle.ffn_relu2(Xq_ref[rows], d_ref[rows], Wgp.cpu().numpy(), gg.item(),
-                           Wup.cpu().numpy() if gated else None, gu.item(),
-                           nw.numpy() if gain else None, eps, Wdp.cpu().numpy(), gd.item(),
+    ref = oracle.ffn_relu2(Xq_ref[rows], d_ref[rows], ref_w["g"][0], ref_w["g"][1],
+                           ref_w["u"][0] if gated else None, ref_w["u"][1],
+                           nw.numpy() if gain else None, eps, ref_w["d"][0], ref_w["d"][1],
                            K, F, N)
     assert np.array_equal(Hq.cpu().numpy()[rows], ref["Hq"])
     assert np.array_equal(_f32_bits(dh.cpu().numpy()[rows]), _f32_bits(ref["dh"]))

@@ -13,7 +13,9 @@ in for trained weights and real token activations):
   * activations X ~ N(0, 1), shape [M, K]; for the decode / batched / prefill
     workloads 1% of the K channels (``randperm(K)[:round(0.01 K)]``, the same
     channels for every token) are scaled by 20 to mimic outlier channels, and
-    X is then rounded to bf16.
+    X is then rounded to bf16;
+  * QAT backward: the output gradient dY ~ N(0, 0.001^2), fp32 [M, N], drawn
+    after W and X from the same generator.
 """
 from dataclasses import dataclass, field
 from typing import List, Tuple
@@ -67,6 +69,24 @@ def ffn_problem(seed: int, M: int, K: int, F: int, N: int, dtype=torch.bfloat16,
     return Wg, Wu, Wd, X
 
 
+GRAD_STD = 1e-3
+
+
+def grad_output(g: torch.Generator, M: int, N: int) -> torch.Tensor:
+    """fp32 output gradient dY [M, N] ~ N(0, 0.001^2)."""
+    return torch.randn(M, N, generator=g, dtype=torch.float32) * GRAD_STD
+
+
+def qat_problem(seed: int, M: int, K: int, N: int, dtype=torch.bfloat16, outliers: bool = True):
+    """(W fp32 [N, K], X [M, K], dY fp32 [M, N]) for one BitLinear's training
+    step, drawn in that order."""
+    g = generator(seed)
+    W = weight(g, N, K)
+    X = activations(g, M, K, dtype=dtype, outliers=outliers)
+    dY = grad_output(g, M, N)
+    return W, X, dY
+
+
 def bf16_bits(X: torch.Tensor):
     """bf16 tensor -> numpy uint16 bit patterns (for the CPU oracle)."""
     return X.contiguous().view(torch.int16).numpy().view("uint16")
@@ -99,6 +119,13 @@ BATCHED_SHAPES: List[Shape] = [
 ]
 
 PREFILL = dict(M=2048, K=2560, F=6912, N=2560, seed=0)
+
+# QAT backward: one 2048-token batch through the FFN's BitLinears.
+QAT_M = 2048
+QAT_SHAPES: List[Shape] = [
+    Shape(2560, 6912, "gate/up 2560->6912"),
+    Shape(6912, 2560, "down 6912->2560"),
+]
 
 HIDDEN = 2560
 KV = 640
