@@ -158,9 +158,10 @@ BL_EXPORT size_t bl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int
         return round_up(bl::stack_ws_floats((int)N, (int)K, (int)F) * sizeof(float), 256);
     case BL_OP_BACKWARD_INPUT:
         if (K < 0 || N < 0 || N > kBackwardMax) return 0;
-        return round_up(bl::backward_input_ws_bytes(N, K), 256);
+        if (M < 0 || M > kBackwardMax) return 0;
+        return round_up(bl::backward_input_ws_bytes(M, N, K), 256);
     case BL_OP_BACKWARD_WEIGHT:
-        if (K < 0 || M < 0 || N < 0 || M > kBackwardMax) return 0;
+        if (K < 0 || M < 0 || N < 0 || M > kBackwardMax || N > kBackwardMax) return 0;
         return round_up(bl::backward_weight_ws_bytes(M, N, K), 256);
     default: return 0;
     }

@@ -9,15 +9,20 @@
 //     dW = dY^T . X~ = (dY o d)^T . Xq        [N][K]
 // Both multiply fp32 gradients by small integers ({-1, 0, +1} or int8
 // codes), which bf16 holds exactly.  Each fp32 value a is split into
-// hi = bf16(a) and lo = bf16(a - hi) (a = hi + lo to about 2^-17 relative)
-// and v_mfma_f32_32x32x16_bf16 takes both halves against the same integer
+// hi = bf16(a) and lo = bf16(a - hi) (a = hi + lo to about 2^-17 relative;
+// both roundings to nearest even, v_cvt_pk_bf16_f32), and
+// v_mfma_f32_32x32x16_bf16 takes both halves against the same integer
 // operand: every product is exact in fp32, only the fp32 accumulation rounds.
 //
-// One product kernel, C[i][j] = s . sum_c A[i][c] B[j][c], A fp32 and B int8,
-// both contraction-contiguous.  Transpose kernels put the operands in that
-// form (rows padded to a multiple of 64, pads written as zeros):
-//     dX:  A = dY [M][N],              B = Wq^T [K][Np],   s = gamma
-//     dW:  A = (dY o d)^T [N][Mp],     B = Xq^T [K][Mp],   s = 1
+// One product kernel, C[i][j] = s . sum_c A[i][c] B[j][c], B bf16 and A
+// either fp32 (split while it is staged into LDS) or already split into two
+// bf16 planes, both operands contraction-contiguous.  Preparation kernels put
+// the operands in that form (rows padded to a multiple of 64, pads written as
+// zeros):
+//     dX:  A = dY [M][N] fp32,                 B = Wq^T [K][Np] bf16,  s = gamma
+//     dW:  A = (dY o d)^T [N][Mp] hi/lo bf16,  B = Xq^T [K][Mp] bf16,  s = 1
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -25,16 +30,32 @@ namespace bl {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTile = 64;                         // transpose tile (elements)
+constexpr int kTile = 64;                         // preparation tile (elements)
 
-// Wq^T [K][ld] (int8) from the packed rows Wp [N][K/4]: tile of 64 rows n x
+// bf16 bits of small integers (|v| <= 127, exact): the top half of the fp32.
+__device__ __forceinline__ uint32_t bf16_of_int(int v) { return __float_as_uint((float)v) >> 16; }
+
+// Two fp32 values -> their bf16 pair (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+    const bf16x2 h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// hi / lo split of two fp32 values: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = cvt_pk(a, b);
+    lo = cvt_pk(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+
+// Wq^T [K][ld] (bf16) from the packed rows Wp [N][K/4]: tile of 64 rows n x
 // 64 weights k; codes {0, 1, 2} -> {0, +1, -1}; columns n >= N are zeros.
 __global__ __launch_bounds__(256) void unpack_transpose_kernel(const uint8_t *__restrict__ Wp, int N,
-                                                               int K, int8_t *__restrict__ WT,
+                                                               int K, uint16_t *__restrict__ WT,
                                                                int ld) {
-    __shared__ int8_t s[kTile][kTile + 16];      // 80-byte rows: 16-byte aligned reads
+    __shared__ uint16_t s[kTile][kTile + 8];     // 144-byte rows: 16-byte aligned reads
     const int t = threadIdx.x;
     const int n0 = blockIdx.x * kTile, k0 = blockIdx.y * kTile;
     {
@@ -45,20 +66,27 @@ __global__ __launch_bounds__(256) void unpack_transpose_kernel(const uint8_t *__
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const uint32_t c = (dw >> (2 * j)) & 3u;
-            s[16 * q + j][r] = (int8_t)((int)(c & 1u) - (int)(c >> 1));
+            s[16 * q + j][r] = (uint16_t)bf16_of_int((int)(c & 1u) - (int)(c >> 1));
         }
     }
     __syncthreads();
-    const int k = t >> 2, seg = t & 3;                    // row k0 + k, 16 columns per segment
-    const uint4 v = *reinterpret_cast<const uint4 *>(&s[k][16 * seg]);
-    *reinterpret_cast<uint4 *>(WT + (size_t)(k0 + k) * ld + n0 + 16 * seg) = v;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int e = t + 256 * p;
+        const int k = e >> 3, seg = e & 7;                // row k0 + k, 8 columns per segment
+        const uint4 v = *reinterpret_cast<const uint4 *>(&s[k][8 * seg]);
+        *reinterpret_cast<uint4 *>(WT + (size_t)(k0 + k) * ld + n0 + 8 * seg) = v;
+    }
 }
 
-// G^T [N][ld] (fp32) = (dY o d)^T: G^T[n][m] = fl(dY[m][n] * d[m]); columns
-// m >= M are zeros.
-__global__ __launch_bounds__(256) void transpose_scale_kernel(const float *__restrict__ dY,
-                                                              const float *__restrict__ d, int M,
-                                                              int N, float *__restrict__ GT, int ld) {
+// (dY o d)^T split into bf16 planes GH, GL [N][ld]: G^T[n][m] = fl(dY[m][n] d[m]),
+// GH = bf16(G^T), GL = bf16(G^T - GH); columns m >= M are zeros.
+__global__ __launch_bounds__(256) void transpose_scale_split_kernel(const float *__restrict__ dY,
+                                                                    const float *__restrict__ d,
+                                                                    int M, int N,
+                                                                    uint16_t *__restrict__ GH,
+                                                                    uint16_t *__restrict__ GL,
+                                                                    int ld) {
     __shared__ float s[kTile][kTile + 1];
     const int t = threadIdx.x;
     const int m0 = blockIdx.x * kTile, n0 = blockIdx.y * kTile;
@@ -72,17 +100,23 @@ __global__ __launch_bounds__(256) void transpose_scale_kernel(const float *__res
     }
     __syncthreads();
 #pragma unroll
-    for (int p = 0; p < kTile * kTile / 256; ++p) {
+    for (int p = 0; p < kTile * kTile / 512; ++p) {
         const int e = t + 256 * p;
-        const int r = e >> 6, c = e & 63;                 // G^T row n0 + r, column m0 + c
-        if (n0 + r < N) GT[(size_t)(n0 + r) * ld + m0 + c] = s[r][c];
+        const int r = e >> 5, c = 2 * (e & 31);           // G^T row n0 + r, columns m0 + c, + 1
+        if (n0 + r < N) {
+            uint32_t hi, lo;
+            split2(s[r][c], s[r][c + 1], hi, lo);
+            const size_t o = (size_t)(n0 + r) * ld + m0 + c;
+            *reinterpret_cast<uint32_t *>(GH + o) = hi;
+            *reinterpret_cast<uint32_t *>(GL + o) = lo;
+        }
     }
 }
 
-// Xq^T [K][ld] (int8); columns m >= M are zeros.
+// Xq^T [K][ld] (bf16); columns m >= M are zeros.
 __global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t *__restrict__ Xq, int M,
-                                                           int K, int8_t *__restrict__ XT, int ld) {
-    __shared__ int8_t s[kTile][kTile + 16];      // 80-byte rows: 16-byte aligned reads
+                                                           int K, uint16_t *__restrict__ XT, int ld) {
+    __shared__ uint16_t s[kTile][kTile + 8];     // 144-byte rows: 16-byte aligned reads
     const int t = threadIdx.x;
     const int m0 = blockIdx.x * kTile, k0 = blockIdx.y * kTile;
     {
@@ -92,137 +126,213 @@ __global__ __launch_bounds__(256) void transpose_i8_kernel(const int8_t *__restr
             v = *reinterpret_cast<const uint4 *>(Xq + (size_t)(m0 + r) * K + k0 + 16 * seg);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s[16 * seg + j][r] = (int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
+        for (int j = 0; j < 16; ++j)
+            s[16 * seg + j][r] = (uint16_t)bf16_of_int((int)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF));
     }
     __syncthreads();
-    const int k = t >> 2, seg = t & 3;
-    const uint4 v = *reinterpret_cast<const uint4 *>(&s[k][16 * seg]);
-    *reinterpret_cast<uint4 *>(XT + (size_t)(k0 + k) * ld + m0 + 16 * seg) = v;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int e = t + 256 * p;
+        const int k = e >> 3, seg = e & 7;
+        const uint4 v = *reinterpret_cast<const uint4 *>(&s[k][8 * seg]);
+        *reinterpret_cast<uint4 *>(XT + (size_t)(k0 + k) * ld + m0 + 8 * seg) = v;
+    }
 }
 
 // ------------------------------------------------------------- the product
-constexpr int kBI = 128, kBJ = 128, kBC = 32;
-constexpr int kLP = kBC + 8;                      // bf16 per staged row (+8 pad: 80 bytes)
+// 128 x 256 tiles of C, 4 waves of 64 x 128 (2 x 4 blocks of 32 x 32); 32-wide
+// c-steps, double-buffered in LDS, the next step's operands loaded while the
+// current one computes.  LDS rows hold 32 bf16 + 8 pad (80 bytes: the 16-byte
+// fragment reads of 16 consecutive rows hit distinct banks).
+constexpr int kTI = 128, kTJ = 256, kBC = 32;
+constexpr int kRowDw = (kBC + 8) / 2;             // dwords per LDS row
+constexpr int kAhiRow = 0, kAloRow = kTI, kBRow = 2 * kTI;
+constexpr int kStageDw = (2 * kTI + kTJ) * kRowDw;
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // finite inputs
-}
-__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
-
-struct StageNT {
-    float4 a[4];                                  // 128 x 32 fp32 of A: 4 float4 per thread
-    uint4 b;                                      // 128 x 32 int8 of B: 16 bytes per thread
+struct Operands {
+    const float *a32;                             // fp32 A, split in the kernel (or null)
+    const uint16_t *ahi, *alo;                    // bf16 planes of A (when a32 is null)
+    int lda;
+    const uint16_t *b;
+    int ldb;
 };
 
-__device__ __forceinline__ void load_nt(StageNT &st, const float *__restrict__ A, int lda,
-                                        const int8_t *__restrict__ B, int ldb, int I, int J, int C,
-                                        int i0, int j0, int c0, int t) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int e = t + 256 * p;
-        const int r = e >> 3, q = e & 7;                  // row i0 + r, columns c0 + 4q .. + 3
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i0 + r < I && c0 + 4 * q < C)                 // C % 4 == 0
-            v = *reinterpret_cast<const float4 *>(A + (size_t)(i0 + r) * lda + c0 + 4 * q);
-        st.a[p] = v;
-    }
-    const int r = t >> 1, h = t & 1;                      // row j0 + r, columns c0 + 16h .. + 15
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (j0 + r < J) v = *reinterpret_cast<const uint4 *>(B + (size_t)(j0 + r) * ldb + c0 + 16 * h);
-    st.b = v;
-}
+template <bool kF32A> struct Staged;
+template <> struct Staged<true> { float4 a[4]; uint4 b[4]; };
+template <> struct Staged<false> { uint4 ah[2], al[2]; uint4 b[4]; };
 
-// A -> hi / lo bf16 planes, B -> bf16 (exact: |b| <= 127), into LDS rows of kLP.
-__device__ __forceinline__ void store_nt(const StageNT &st, uint32_t *Ahi, uint32_t *Alo, uint32_t *Bs,
-                                         int t) {
+// Branch-free loads: rows past I (J) read row I - 1 (J - 1), whose products
+// land only in outputs that are never stored; fp32 columns past C read column
+// C - 4, and meet B's zero pad columns.  Planes and B have zero pad columns
+// up to the row length, a multiple of 64.
+template <bool kF32A>
+__device__ __forceinline__ void load_stage(Staged<kF32A> &st, const Operands &op, int I, int J, int C,
+                                           int i0, int j0, int c0, int t) {
+    if constexpr (kF32A) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int e = t + 256 * p;
-        const int r = e >> 3, q = e & 7;
-        const float x[4] = {st.a[p].x, st.a[p].y, st.a[p].z, st.a[p].w};
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            hi[u] = bf16_rne(x[u]);
-            lo[u] = bf16_rne(x[u] - __uint_as_float(hi[u] << 16));   // exact difference
+        for (int p = 0; p < 4; ++p) {
+            const int e = t + 256 * p;
+            const int r = e >> 3, q = e & 7;              // row i0 + r, columns c0 + 4q .. + 3
+            const int rr = min(i0 + r, I - 1), cc = min(c0 + 4 * q, C - 4);
+            st.a[p] = *reinterpret_cast<const float4 *>(op.a32 + (size_t)rr * op.lda + cc);
         }
-        uint32_t *ph = Ahi + r * (kLP / 2) + 2 * q;
-        uint32_t *pl = Alo + r * (kLP / 2) + 2 * q;
-        *reinterpret_cast<uint2 *>(ph) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-        *reinterpret_cast<uint2 *>(pl) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
-    }
-    const int r = t >> 1, h = t & 1;
-    const uint32_t w[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
-    uint32_t o[8];
+    } else {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int b0 = (int)(int8_t)((w[u >> 1] >> (16 * (u & 1))) & 0xFF);
-        const int b1 = (int)(int8_t)((w[u >> 1] >> (16 * (u & 1) + 8)) & 0xFF);
-        o[u] = pack2(__float_as_uint((float)b0) >> 16, __float_as_uint((float)b1) >> 16);
+        for (int p = 0; p < 2; ++p) {
+            const int e = t + 256 * p;
+            const int r = e >> 2, q = e & 3;              // row i0 + r, columns c0 + 8q .. + 7
+            const size_t o = (size_t)min(i0 + r, I - 1) * op.lda + c0 + 8 * q;
+            const uint4 h = *reinterpret_cast<const uint4 *>(op.ahi + o);
+            const uint4 l = *reinterpret_cast<const uint4 *>(op.alo + o);
+            st.ah[p] = h;
+            st.al[p] = l;
+        }
     }
-    uint4 *pb = reinterpret_cast<uint4 *>(Bs + r * (kLP / 2) + 8 * h);
-    pb[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    pb[1] = make_uint4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int e = t + 256 * p;
+        const int r = e >> 2, q = e & 3;                  // row j0 + r, columns c0 + 8q .. + 7
+        const uint4 v = *reinterpret_cast<const uint4 *>(op.b + (size_t)min(j0 + r, J - 1) * op.ldb +
+                                                         c0 + 8 * q);
+        st.b[p] = v;
+    }
 }
 
-// C[i][j] = s . sum_{c < C} A[i][c] B[j][c]; 128 x 128 tiles, 4 waves of
-// 64 x 64 (2 x 2 blocks of 32 x 32); 32-wide c-steps, LDS double-buffered,
-// the next step's operands loaded while the current one computes.
-__global__ __launch_bounds__(256) void gemm_nt_f32i8_kernel(
-    const float *__restrict__ A, int lda, const int8_t *__restrict__ B, int ldb, int I, int J, int C,
-    const float *__restrict__ scale, float *__restrict__ Out, int ldo) {
-    constexpr int kPlane = kBI * kLP / 2;                 // dwords per 128-row bf16 plane
-    __shared__ uint32_t lds[2][3][kPlane];                // [buffer][A hi, A lo, B]
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wi = wave >> 1, wj = wave & 1;
-    const int i0 = blockIdx.x * kBI, j0 = blockIdx.y * kBJ;
-    const int steps = (C + kBC - 1) / kBC;
+template <bool kF32A>
+__device__ __forceinline__ void store_stage(const Staged<kF32A> &st, uint32_t *lds, int t) {
+    if constexpr (kF32A) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int e = t + 256 * p;
+            const int r = e >> 3, q = e & 7;
+            uint32_t h0, l0, h1, l1;
+            split2(st.a[p].x, st.a[p].y, h0, l0);
+            split2(st.a[p].z, st.a[p].w, h1, l1);
+            *reinterpret_cast<uint2 *>(lds + (kAhiRow + r) * kRowDw + 2 * q) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2 *>(lds + (kAloRow + r) * kRowDw + 2 * q) = make_uint2(l0, l1);
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int e = t + 256 * p;
+            const int r = e >> 2, q = e & 3;
+            *reinterpret_cast<uint4 *>(lds + (kAhiRow + r) * kRowDw + 4 * q) = st.ah[p];
+            *reinterpret_cast<uint4 *>(lds + (kAloRow + r) * kRowDw + 4 * q) = st.al[p];
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int e = t + 256 * p;
+        const int r = e >> 2, q = e & 3;
+        *reinterpret_cast<uint4 *>(lds + (kBRow + r) * kRowDw + 4 * q) = st.b[p];
+    }
+}
 
-    f32x16 acc[2][2];
+__device__ __forceinline__ bf16x8 frag(const uint32_t *lds, int row, int col) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(lds + row * kRowDw + col));
+}
+
+// Tile order: the 8 XCDs receive workgroups round-robin; each XCD takes a
+// contiguous run of row-major tiles, so the row panels of A it streams stay
+// in its own L2.
+__device__ __forceinline__ int xcd_tile(int L, int T) {
+    const int q = T / 8, rem = T % 8, x = L % 8;
+    return x * q + min(x, rem) + L / 8;
+}
+
+struct Frags {
+    bf16x8 ah[2], al[2], bb[4];
+};
+
+// One 16-wide sub-step's fragments of a wave: A hi / lo rows arow + 32a and B
+// rows brow + 32b, columns col .. col + 3 (dwords).
+__device__ __forceinline__ void read_frags(Frags &f, const uint32_t *L, int arow, int brow, int col) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        f.ah[a] = frag(L, kAhiRow + arow + 32 * a, col);
+        f.al[a] = frag(L, kAloRow + arow + 32 * a, col);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f.bb[b] = frag(L, brow + 32 * b, col);
+}
+
+__device__ __forceinline__ void mfma_substep(f32x16 (&acc)[2][4], const Frags &f) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+        for (int b = 0; b < 4; ++b) {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[a], f.bb[b], acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.al[a], f.bb[b], acc[a][b], 0, 0, 0);
+        }
+}
 
-    StageNT st;
+// kPipe: sub-step 1's fragments are read before sub-step 0's MFMAs, and the
+// next step's sub-step 0 fragments right after the barrier, under sub-step
+// 1's MFMAs, so LDS latency hides behind matrix work.  It needs both
+// sub-steps' fragments live, which with fp32 A does not fit two workgroups
+// per CU; both loops add the same products in the same order.
+//
+// Contraction split: unit u of the grid is tile u % T (T tiles) over the
+// c-steps [z split_steps, (z + 1) split_steps) of z = u / T.  With one split
+// it stores s . C to Out; with several it stores its raw partial sum to
+// Out + z split_stride and split_sum_kernel adds them.
+template <bool kF32A, bool kPipe>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16x2_kernel(
+    const Operands op, int I, int J, int C, int tiles, int tiles_j, int split_steps,
+    size_t split_stride, const float *__restrict__ scale, float *__restrict__ Out, int ldo) {
+    __shared__ uint32_t lds[2 * kStageDw];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wi = wave >> 1, wj = wave & 1;
+    const int u = xcd_tile(blockIdx.x, gridDim.x);
+    const int z = u / tiles, tile = u - z * tiles;
+    const int i0 = (tile / tiles_j) * kTI, j0 = (tile % tiles_j) * kTJ;
+    const int cb = z * split_steps * kBC;                 // first column of this split
+    const int steps = min(split_steps, (C + kBC - 1) / kBC - z * split_steps);
+    Out += z * split_stride;
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+
+    const int arow = wi * 64 + (lane & 31), brow = kBRow + wj * 128 + (lane & 31);
+    const int col0 = 4 * (lane >> 5), col1 = 8 + 4 * (lane >> 5);
+    Staged<kF32A> st;
     if (steps > 0) {
-        load_nt(st, A, lda, B, ldb, I, J, C, i0, j0, 0, t);
-        store_nt(st, lds[0][0], lds[0][1], lds[0][2], t);
-        if (steps > 1) load_nt(st, A, lda, B, ldb, I, J, C, i0, j0, kBC, t);
+        load_stage<kF32A>(st, op, I, J, C, i0, j0, cb, t);
+        store_stage<kF32A>(st, lds, t);
+        if (steps > 1) load_stage<kF32A>(st, op, I, J, C, i0, j0, cb + kBC, t);
     }
     __syncthreads();
-    for (int s = 0; s < steps; ++s) {
-        const int buf = s & 1;
-        const uint32_t *Ahi = lds[buf][0], *Alo = lds[buf][1], *Bs = lds[buf][2];
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {               // 16 c per MFMA
-            const int col = (16 * sub + 8 * (lane >> 5)) / 2;      // dword offset in a row
-            bf16x8 ah[2], al[2], bb[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const int row = wi * 64 + a * 32 + (lane & 31);
-                ah[a] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Ahi + row * (kLP / 2) + col));
-                al[a] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Alo + row * (kLP / 2) + col));
+    if constexpr (kPipe) {
+        Frags f0, f1;
+        if (steps > 0) read_frags(f0, lds, arow, brow, col0);
+        for (int s = 0; s < steps; ++s) {
+            read_frags(f1, lds + (s & 1) * kStageDw, arow, brow, col1);
+            mfma_substep(acc, f0);
+            if (s + 1 < steps) {
+                store_stage<kF32A>(st, lds + ((s + 1) & 1) * kStageDw, t);
+                if (s + 2 < steps) load_stage<kF32A>(st, op, I, J, C, i0, j0, cb + (s + 2) * kBC, t);
             }
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int row = wj * 64 + b * 32 + (lane & 31);
-                bb[b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Bs + row * (kLP / 2) + col));
+            __syncthreads();
+            if (s + 1 < steps) read_frags(f0, lds + ((s + 1) & 1) * kStageDw, arow, brow, col0);
+            mfma_substep(acc, f1);
+        }
+    } else {
+        for (int s = 0; s < steps; ++s) {
+            const uint32_t *L = lds + (s & 1) * kStageDw;
+            Frags f;
+            read_frags(f, L, arow, brow, col0);
+            mfma_substep(acc, f);
+            read_frags(f, L, arow, brow, col1);
+            mfma_substep(acc, f);
+            if (s + 1 < steps) {
+                store_stage<kF32A>(st, lds + ((s + 1) & 1) * kStageDw, t);
+                if (s + 2 < steps) load_stage<kF32A>(st, op, I, J, C, i0, j0, cb + (s + 2) * kBC, t);
             }
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bb[b], acc[a][b], 0, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[a], bb[b], acc[a][b], 0, 0, 0);
-                }
+            __syncthreads();
         }
-        if (s + 1 < steps) {
-            store_nt(st, lds[buf ^ 1][0], lds[buf ^ 1][1], lds[buf ^ 1][2], t);
-            if (s + 2 < steps) load_nt(st, A, lda, B, ldb, I, J, C, i0, j0, (s + 2) * kBC, t);
-        }
-        __syncthreads();
     }
 
     const float sc = scale ? scalar_load(scale) : 1.0f;
@@ -233,11 +343,81 @@ __global__ __launch_bounds__(256) void gemm_nt_f32i8_kernel(
             const int i = i0 + wi * 64 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if (i >= I) continue;
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int j = j0 + wj * 64 + b * 32 + (lane & 31);
+            for (int b = 0; b < 4; ++b) {
+                const int j = j0 + wj * 128 + b * 32 + (lane & 31);
                 if (j < J) Out[(size_t)i * ldo + j] = scale ? __fmul_rn(acc[a][b][r], sc) : acc[a][b][r];
             }
         }
+}
+
+constexpr int kCUs = 256;
+
+// Adds the partial sums of the contraction splits in split order, then
+// scales: Out[e] = s . (((P0[e] + P1[e]) + P2[e]) + ...), 4 elements a lane.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ P, int splits,
+                                                        size_t stride, size_t n4,
+                                                        const float *__restrict__ scale,
+                                                        float *__restrict__ Out) {
+    const float sc = scale ? scalar_load(scale) : 1.0f;
+    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n4; e += (size_t)gridDim.x * 256) {
+        float4 a = reinterpret_cast<const float4 *>(P)[e];
+        for (int z = 1; z < splits; ++z) {
+            const float4 b = reinterpret_cast<const float4 *>(P + z * stride)[e];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        if (scale) {
+            a.x = __fmul_rn(a.x, sc);
+            a.y = __fmul_rn(a.y, sc);
+            a.z = __fmul_rn(a.z, sc);
+            a.w = __fmul_rn(a.w, sc);
+        }
+        reinterpret_cast<float4 *>(Out)[e] = a;
+    }
+}
+
+// Contraction splits of an I x J x C product: while the tiles leave CUs idle
+// (at most one per CU), up to 4 splits of at least 8 c-steps each, aiming at
+// two units per CU.  The same rule sizes the workspace.
+struct Split {
+    int splits, split_steps;
+};
+Split choose_split(int64_t I, int64_t J, int64_t C) {
+    const int64_t tiles = ((I + kTI - 1) / kTI) * ((J + kTJ - 1) / kTJ);
+    const int64_t steps = (C + kBC - 1) / kBC;
+    if (steps == 0)
+        return Split{1, 0};
+    int64_t s = 1;
+    if (tiles <= kCUs && steps >= 16)
+        s = std::max<int64_t>(1, std::min<int64_t>({4, 2 * kCUs / tiles, steps / 8}));
+    const int64_t per = (steps + s - 1) / s;
+    return Split{(int)((steps + per - 1) / per), (int)per};
+}
+
+// fp32 A: the plain loop; bf16 planes: the pipelined loop.  `part` holds
+// splits x I x ldo floats when the product is split.
+template <bool kF32A>
+hipError_t launch_product(const Operands &op, int I, int J, int C, const float *scale, float *Out,
+                          int ldo, float *part, hipStream_t s) {
+    const int64_t ti = (I + kTI - 1) / kTI, tj = (J + kTJ - 1) / kTJ;
+    const Split sp = choose_split(I, J, C);
+    if (ti * tj * sp.splits > INT32_MAX)
+        return hipErrorInvalidConfiguration;      // more units than a 1-D grid holds
+    const dim3 grid((unsigned)(ti * tj * sp.splits)), block(256);
+    float *dst = sp.splits > 1 ? part : Out;
+    const float *sc = sp.splits > 1 ? nullptr : scale;
+    const size_t stride = (size_t)I * ldo;
+    hipLaunchKernelGGL((gemm_bf16x2_kernel<kF32A, !kF32A>), grid, block, 0, s, op, I, J, C,
+                       (int)(ti * tj), (int)tj, sp.split_steps, stride, sc, dst, ldo);
+    if (sp.splits > 1) {
+        const size_t n4 = stride / 4;             // ldo == J, a multiple of 64
+        const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 8 * kCUs);
+        hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), block, 0, s, part, sp.splits, stride, n4,
+                           scale, Out);
+    }
+    return hipGetLastError();
 }
 
 int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
@@ -245,11 +425,20 @@ size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t backward_input_ws_bytes(int64_t N, int64_t K) { return (size_t)K * (size_t)pad64(N); }
+// Partial sums of a split product, I x J floats per split (none unsplit).
+size_t partial_bytes(int64_t I, int64_t J, int64_t C) {
+    const Split sp = choose_split(I, J, C);
+    return sp.splits > 1 ? (size_t)sp.splits * (size_t)I * (size_t)J * 4 : 0;
+}
+
+size_t backward_input_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    return round256((size_t)K * (size_t)pad64(N) * 2) + partial_bytes(M, K, N);
+}
 
 size_t backward_weight_ws_bytes(int64_t M, int64_t N, int64_t K) {
     const size_t mp = (size_t)pad64(M);
-    return round256((size_t)N * mp * 4) + (size_t)K * mp;
+    return 2 * round256((size_t)N * mp * 2) + round256((size_t)K * mp * 2) +
+           partial_bytes(N, K, (int64_t)mp);
 }
 
 // Sizes as validated by the entry points: M, N < 2^31 - 63, K % 64 == 0.
@@ -260,13 +449,13 @@ hipError_t launch_backward_input(const float *dY, int M, int N, const uint8_t *W
     if (M == 0 || K == 0)
         return hipSuccess;
     const int np = (int)pad64(N);
-    int8_t *WT = static_cast<int8_t *>(ws);
+    uint16_t *WT = static_cast<uint16_t *>(ws);
     if (np > 0)
         hipLaunchKernelGGL(unpack_transpose_kernel, dim3(np / kTile, K / kTile), dim3(256), 0, s, Wp,
                            N, K, WT, np);
-    hipLaunchKernelGGL(gemm_nt_f32i8_kernel, dim3((M + kBI - 1) / kBI, (K + kBJ - 1) / kBJ), dim3(256),
-                       0, s, dY, N, WT, np, M, K, N, np > 0 ? gamma : nullptr, dX, K);
-    return hipGetLastError();
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + round256((size_t)K * np * 2));
+    const Operands op{dY, nullptr, nullptr, N, WT, np};
+    return launch_product<true>(op, M, K, N, np > 0 ? gamma : nullptr, dX, K, part, s);
 }
 
 hipError_t launch_backward_weight(const float *dY, int M, int N, const int8_t *Xq, const float *d,
@@ -274,17 +463,20 @@ hipError_t launch_backward_weight(const float *dY, int M, int N, const int8_t *X
     if (N == 0 || K == 0)
         return hipSuccess;
     const int mp = (int)pad64(M);
-    float *GT = static_cast<float *>(ws);
-    int8_t *XT = static_cast<int8_t *>(ws) + round256((size_t)N * mp * 4);
+    const size_t plane = round256((size_t)N * mp * 2);
+    uint16_t *GH = static_cast<uint16_t *>(ws);
+    uint16_t *GL = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + plane);
+    uint16_t *XT = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + 2 * plane);
     if (mp > 0) {
-        hipLaunchKernelGGL(transpose_scale_kernel, dim3(mp / kTile, (N + kTile - 1) / kTile), dim3(256),
-                           0, s, dY, d, M, N, GT, mp);
+        hipLaunchKernelGGL(transpose_scale_split_kernel, dim3(mp / kTile, (N + kTile - 1) / kTile),
+                           dim3(256), 0, s, dY, d, M, N, GH, GL, mp);
         hipLaunchKernelGGL(transpose_i8_kernel, dim3(mp / kTile, K / kTile), dim3(256), 0, s, Xq, M, K,
                            XT, mp);
     }
-    hipLaunchKernelGGL(gemm_nt_f32i8_kernel, dim3((N + kBI - 1) / kBI, (K + kBJ - 1) / kBJ), dim3(256),
-                       0, s, GT, mp, XT, mp, N, K, mp, nullptr, dW, K);
-    return hipGetLastError();
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * plane +
+                                            round256((size_t)K * mp * 2));
+    const Operands op{nullptr, GH, GL, mp, XT, mp};
+    return launch_product<false>(op, N, K, mp, nullptr, dW, K, part, s);
 }
 
 }  // namespace bl

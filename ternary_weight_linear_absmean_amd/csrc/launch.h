@@ -80,7 +80,7 @@ hipError_t launch_ffn_tail_z(const float *Z, const float *pmax, const double *ps
 
 // QAT backward (backward.hip): dX = gamma (dY . Wq) and dW = (dY o d)^T . Xq
 // on bf16 MFMA; the workspace holds the transposed operands.
-size_t backward_input_ws_bytes(int64_t N, int64_t K);
+size_t backward_input_ws_bytes(int64_t M, int64_t N, int64_t K);
 size_t backward_weight_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_backward_input(const float *dY, int M, int N, const uint8_t *Wp, const float *gamma,
                                  int K, float *dX, void *ws, hipStream_t s);

@@ -95,8 +95,9 @@ def _check_case(gpu, M, K, N, seed, dtype=torch.bfloat16):
     (3, 192, 68),        # N % 32 = 4: a partial 32-wide contraction step
     (130, 320, 260),     # ragged in every dimension, several tiles
     (257, 128, 132),     # M just past two row tiles
-    (64, 640, 2560),     # k/v's shape transposed: long contraction for dX
-    (200, 2560, 640),    # k/v projection
+    (64, 640, 2560),     # long contraction, 3 tiles: dX split 4 ways
+    (200, 2560, 640),    # k/v projection: dX split 2 ways
+    (1000, 320, 200),    # many tokens, few tiles: dW split 4 ways
 ])
 def test_backward_ragged(gpu, M, K, N):
     _check_case(gpu, M, K, N, 500 + M)
@@ -203,3 +204,19 @@ def test_backward_rejects_bad_shapes(gpu):
         gpu.bitlinear_backward_weight(torch.zeros(2, 8, device="cuda"),
                                       torch.zeros(2, 96, dtype=torch.int8, device="cuda"),
                                       torch.ones(2, device="cuda"))         # K % 64
+
+
+def test_backward_split_products_are_deterministic(gpu):
+    """Products split along the contraction add their partial sums in a
+    fixed order: repeated calls give identical bits."""
+    for M, K, N in ((64, 640, 2560), (1000, 320, 200)):
+        W, X, dY = workloads.qat_problem(590 + M, M, K, N)
+        Wp, g = gpu.quant_weight_absmean_pack(W.cuda())
+        Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+        dYc = dY.cuda()
+        a = [gpu.bitlinear_backward_input(dYc, Wp, g) for _ in range(3)]
+        b = [gpu.bitlinear_backward_weight(dYc, Xq, d) for _ in range(3)]
+        torch.cuda.synchronize()
+        for r in (1, 2):
+            assert torch.equal(a[0].view(torch.int32), a[r].view(torch.int32))
+            assert torch.equal(b[0].view(torch.int32), b[r].view(torch.int32))
