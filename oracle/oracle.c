@@ -37,6 +37,7 @@
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <string.h>
 
@@ -50,21 +51,49 @@ OB_EXPORT int ob_num_threads(void) { return omp_get_max_threads(); }
  *
  * n runs over every element of the weight tensor, so gamma is one number per
  * BitLinear weight matrix W[N][K] (nn.Linear layout: N outputs, K inputs).
- * The pages give no precision or order for the sum.  Reading taken: sum in
- * fp64, each row in ascending k, then the row sums in ascending n; divide by
- * n in fp64; round once to fp32.  A fixed order makes gamma reproducible to
- * the bit.  An empty tensor (n == 0) gets gamma = 0. */
+ * The pages give no precision or order for the sum.  Reading taken: the sum
+ * is in fp64, in one fixed order that parallel hardware can follow:
+ *   - within row n, element k goes to partial (k / 4) mod 64, and each of the
+ *     64 partials adds its elements in ascending k;
+ *   - the 64 partials are added in consecutive pairs, level by level
+ *     (p0 + p1, p2 + p3, ..., then (p0 + p1) + (p2 + p3), ...);
+ *   - the N row sums, extended with zeros to a power of two, are added in
+ *     consecutive pairs in the same way.
+ * Divide by n in fp64; round once to fp32.  Every term is >= 0, so added
+ * zeros change nothing and any longer zero extension gives the same bits.
+ * A fixed order makes gamma reproducible to the bit.  An empty tensor
+ * (n == 0) gets gamma = 0. */
+
+/* Consecutive-pair sum of v[0 .. count), count a power of two; overwrites v. */
+static double pairwise_sum(double *v, int64_t count)
+{
+    for (int64_t h = 1; h < count; h *= 2)
+        for (int64_t i = 0; i + h < count; i += 2 * h)
+            v[i] += v[i + h];
+    return v[0];
+}
+
 OB_EXPORT float ob_absmean_gamma(const float *W, int64_t N, int64_t K)
 {
     if (N <= 0 || K <= 0)
         return 0.0f;
-    double total = 0.0;
+    int64_t P = 1;
+    while (P < N)
+        P *= 2;
+    double *rows = (double *)calloc((size_t)P, sizeof(double));
+    if (!rows)
+        return NAN;
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
-        double row = 0.0;
+        double part[64];
+        for (int l = 0; l < 64; ++l)
+            part[l] = 0.0;
         for (int64_t k = 0; k < K; ++k)
-            row += fabs((double)W[n * K + k]);
-        total += row;
+            part[(k / 4) % 64] += fabs((double)W[n * K + k]);
+        rows[n] = pairwise_sum(part, 64);
     }
+    const double total = pairwise_sum(rows, P);
+    free(rows);
     return (float)(total / (double)(N * K));
 }
 

@@ -22,7 +22,11 @@ from oracle.build import CFLAGS  # noqa: E402
 
 # (name, original text, replacement) -- each original must occur in oracle.c
 MUTANTS = [
-    ("gamma_drops_abs", "row += fabs((double)W[n * K + k]);", "row += ((double)W[n * K + k]);"),
+    ("gamma_drops_abs", "part[(k / 4) % 64] += fabs((double)W[n * K + k]);",
+     "part[(k / 4) % 64] += ((double)W[n * K + k]);"),
+    ("gamma_pairwise_drops_left", "v[i] += v[i + h];", "v[i] = v[i + h];"),
+    ("gamma_skips_last_row", "for (int64_t n = 0; n < N; ++n) {\n        double part[64];",
+     "for (int64_t n = 0; n < N - 1; ++n) {\n        double part[64];"),
     ("gamma_wrong_n", "total / (double)(N * K)", "total / (double)(N * K + 1)"),
     ("round_ties_away", "Wq[i] = (int8_t)nearbyint(t);", "Wq[i] = (int8_t)round(t);"),
     ("no_clamp", "if (t > 1.0) t = 1.0;", ""),
