@@ -250,10 +250,12 @@ def bench_ffn(bl, torch, workloads, steps, warmup):
 
 
 def bench_qat(bl, torch, workloads, steps, warmup):
-    """QAT backward at M = 2048 tokens for the FFN shapes: dX and dW, each
-    timed over back-to-back calls (transposes + product) between two events.
-    TFLOPs counts the 2 M N K algorithmic flops of each gradient; the bf16
-    MFMA issues twice that (the hi and lo halves of the fp32 gradient)."""
+    """QAT at M = 2048 tokens for the FFN shapes: dX and dW, each timed over
+    back-to-back calls (operand preparation + product) between two events,
+    the absmean weight quantiser, and a whole training step of the layer
+    (fresh absmean weights, activation quant, forward, dX, dW).  TFLOPs
+    counts the 2 M N K algorithmic flops of each gradient; the bf16 MFMA
+    issues twice that (the hi and lo halves of the fp32 gradient)."""
     out = []
     for sh in workloads.QAT_SHAPES:
         M, K, N = workloads.QAT_M, sh.K, sh.N
@@ -267,9 +269,27 @@ def bench_qat(bl, torch, workloads, steps, warmup):
                           dtype=torch.uint8, device="cuda")
         wsw = torch.empty((bl.workspace_bytes(bl.BL_OP_BACKWARD_WEIGHT, M, N, K),),
                           dtype=torch.uint8, device="cuda")
+        Wd = W.cuda()
+        Xd = X.cuda()
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        wsq = torch.empty((max(16, bl.workspace_bytes(bl.BL_OP_QUANT_WEIGHT, 0, N, K)),),
+                          dtype=torch.uint8, device="cuda")
+
+        def step():
+            # one training step of the layer: fresh absmean weights, per-token
+            # activations, forward, both straight-through gradients
+            bl.quant_weight_absmean_pack(Wd, Wp=Wp, gamma=g, ws=wsq)
+            bl.quant_act_absmax_i8(Xd, Xq=Xq, d=d)
+            bl.bitlinear_gemm(Xq, d, Wp, g, Y=Y)
+            bl.bitlinear_backward_input(dY, Wp, g, dX=dX, ws=wsi)
+            bl.bitlinear_backward_weight(dY, Xq, d, dW=dW, ws=wsw)
+
         row = dict(M=M, K=K, N=N)
         for name, fn in (("dX", lambda: bl.bitlinear_backward_input(dY, Wp, g, dX=dX, ws=wsi)),
-                         ("dW", lambda: bl.bitlinear_backward_weight(dY, Xq, d, dW=dW, ws=wsw))):
+                         ("dW", lambda: bl.bitlinear_backward_weight(dY, Xq, d, dW=dW, ws=wsw)),
+                         ("weight_quant", lambda: bl.quant_weight_absmean_pack(Wd, Wp=Wp, gamma=g,
+                                                                               ws=wsq)),
+                         ("step", step)):
             for _ in range(warmup):
                 fn()
             torch.cuda.synchronize()
@@ -281,9 +301,16 @@ def bench_qat(bl, torch, workloads, steps, warmup):
             t1.record()
             torch.cuda.synchronize()
             us = 1000.0 * t0.elapsed_time(t1) / steps
-            tf = 2.0 * M * N * K / us / 1e6
-            row[name] = dict(us=round(us, 2), TFLOPs=round(tf, 1),
-                             mfma_frac_bf16=round(2.0 * tf / BF16_MFMA_PEAK_TFLOPS, 4))
+            if name in ("dX", "dW"):
+                tf = 2.0 * M * N * K / us / 1e6
+                row[name] = dict(us=round(us, 2), TFLOPs=round(tf, 1),
+                                 mfma_frac_bf16=round(2.0 * tf / BF16_MFMA_PEAK_TFLOPS, 4))
+            elif name == "weight_quant":
+                # fp32 W read twice (sum, then ternarise) + packed codes written
+                byts = 2 * 4 * N * K + N * K // 4
+                row[name] = dict(us=round(us, 2), GBs=round(byts / us / 1e3, 1))
+            else:
+                row[name] = dict(us=round(us, 2))
         out.append(row)
     return out
 

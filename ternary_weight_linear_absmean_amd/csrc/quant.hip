@@ -13,85 +13,102 @@ namespace bl {
 namespace {
 
 // ---------------------------------------------------------------------------
-// gamma, step 1: fp64 sum of |W[n][k]| over k in ascending order, one row per
-// thread.  A wave stages a 64-row x 64-column tile through LDS (coalesced
-// float4 loads, 16 per thread), then each thread adds its row's 64 values in
-// k order.  The next tile's loads are all issued before the current tile is
-// summed, so memory latency overlaps the (inherently sequential) fp64 adds.
-// Tail columns are read as 0, and adding +0.0 to a non-negative sum is
-// exact, so the result is the plain ascending-k sum.
-constexpr int kRowsumRows = 64;
-constexpr int kRowsumCols = 64;
-constexpr int kRowsumLoads = kRowsumRows * (kRowsumCols / 4) / 64;   // float4 per thread
+// gamma = (1/n) sum |W| in fp64, in one fixed order (the pages fix none):
+// within a row, element k goes to partial (k / 4) mod 64 and each partial adds
+// its elements in ascending k; the 64 partials are added in consecutive pairs,
+// level by level; the row sums, zero-extended to a power of two, are added in
+// consecutive pairs the same way; then / n in fp64 and one rounding to fp32.
+// Every term is >= 0, so adding +0.0 (tails, padding) changes nothing.
 
-__global__ __launch_bounds__(64) void rowsum_abs_kernel(const float *__restrict__ W, int64_t N,
-                                                        int64_t K, double *__restrict__ rowsum) {
-    __shared__ float tile[kRowsumRows][kRowsumCols + 1];
-    const int t = threadIdx.x;
-    const int64_t n0 = (int64_t)blockIdx.x * kRowsumRows;
-    // thread t's float4 i covers row (t + 64 i) / 16, columns 4 ((t + 64 i) % 16)..+3
-    auto load_tile = [&](int64_t k0, float4 (&v)[kRowsumLoads]) {
+// Row sums, one wave per row: lane l is partial l, reading the float4 units
+// l, l + 64, ... of its row (coalesced, eight units in flight), and the
+// partials are added in consecutive pairs by shuffles (after the step with
+// offset h, lane i * 2h holds the pair sum of its 2h-lane group).
+constexpr int kRowsumWaves = 4;
+constexpr int kRowsumUnroll = 8;
+
+__global__ __launch_bounds__(64 * kRowsumWaves) void rowsum_abs_kernel(const float *__restrict__ W,
+                                                                       int64_t N, int64_t K,
+                                                                       double *__restrict__ rowsum) {
+    const int lane = threadIdx.x & 63;
+    const int64_t n = (int64_t)blockIdx.x * kRowsumWaves + (threadIdx.x >> 6);
+    if (n >= N)
+        return;                                   // whole wave; no barrier follows
+    const float *row = W + n * K;
+    const int64_t units = K / 4;                  // K % 4 == 0
+    double p = 0.0;
+    for (int64_t u0 = lane; u0 < units; u0 += 64 * kRowsumUnroll) {
+        float4 v[kRowsumUnroll];
 #pragma unroll
-        for (int i = 0; i < kRowsumLoads; ++i) {
-            const int j = t + 64 * i;
-            const int64_t n = n0 + j / (kRowsumCols / 4);
-            const int64_t k = k0 + 4 * (j % (kRowsumCols / 4));
-            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (n < N && k < K)   // K % 4 == 0, so a float4 never straddles K
-                v[i] = *reinterpret_cast<const float4 *>(W + n * K + k);
+        for (int i = 0; i < kRowsumUnroll; ++i) {
+            const int64_t u = u0 + 64 * i;
+            v[i] = u < units ? *reinterpret_cast<const float4 *>(row + 4 * u)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    };
-    float4 v[kRowsumLoads];
-    load_tile(0, v);
-    double sum = 0.0;
-    for (int64_t k0 = 0; k0 < K; k0 += kRowsumCols) {
 #pragma unroll
-        for (int i = 0; i < kRowsumLoads; ++i) {
-            const int j = t + 64 * i;
-            const int r = j / (kRowsumCols / 4), c = 4 * (j % (kRowsumCols / 4));
-            tile[r][c + 0] = v[i].x;
-            tile[r][c + 1] = v[i].y;
-            tile[r][c + 2] = v[i].z;
-            tile[r][c + 3] = v[i].w;
+        for (int i = 0; i < kRowsumUnroll; ++i) {
+            p += fabs((double)v[i].x);
+            p += fabs((double)v[i].y);
+            p += fabs((double)v[i].z);
+            p += fabs((double)v[i].w);
         }
-        __syncthreads();
-        if (k0 + kRowsumCols < K) load_tile(k0 + kRowsumCols, v);
-        for (int c = 0; c < kRowsumCols; ++c)
-            sum += fabs((double)tile[t][c]);
-        __syncthreads();
     }
-    const int64_t n = n0 + t;
-    if (n < N)
-        rowsum[n] = sum;
+#pragma unroll
+    for (int h = 1; h < 64; h *= 2) p += __shfl_down(p, h);
+    if (lane == 0)
+        rowsum[n] = p;
 }
 
-// gamma, step 2: add the row sums in ascending n, divide by n in fp64, round
-// once to fp32.  The wave stages chunks of row sums in LDS (all loads of a
-// chunk in flight together) and lane 0 adds them in order.
-constexpr int kGammaChunk = 2048;
+// Total: one workgroup of 1024 threads takes the row sums in chunks of 8192
+// (thread t: 8 consecutive values, added in pairs in registers; then lanes by
+// shuffles; then the 16 wave sums in wave 0) -- each chunk sum is a subtree
+// of the zero-extended pair tree.  The chunk sums are combined with a carry
+// stack, as in binary counting: chunk c is pushed, and while the subtree at
+// the top has a left sibling of the same size they are added, left + right.
+// At the end the stack is folded from the top (a missing right sibling is a
+// zero subtree, and x + 0 = x).
+constexpr int kGammaThreads = 1024;
+constexpr int kGammaChunk = 8 * kGammaThreads;
 
-__global__ __launch_bounds__(64) void gamma_kernel(const double *__restrict__ rowsum, int64_t N,
-                                                   int64_t K, float *__restrict__ gamma) {
-    __shared__ double buf[kGammaChunk];
-    const int lane = threadIdx.x;
-    double total = 0.0;
-    for (int64_t c0 = 0; c0 < N; c0 += kGammaChunk) {
-        const int cnt = (N - c0) < kGammaChunk ? (int)(N - c0) : kGammaChunk;
-        double v[kGammaChunk / 64];
+__global__ __launch_bounds__(kGammaThreads) void gamma_kernel(const double *__restrict__ rowsum,
+                                                              int64_t N, int64_t K,
+                                                              float *__restrict__ gamma) {
+    __shared__ double wsum[kGammaThreads / 64];
+    __shared__ double stack[48];                  // thread 0's carry stack, one entry per level
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int depth = 0;                                // meaningful in thread 0
+    const int64_t chunks = (N + kGammaChunk - 1) / kGammaChunk;
+    for (int64_t c = 0; c < chunks; ++c) {
+        double e[8];
 #pragma unroll
-        for (int i = 0; i < kGammaChunk / 64; ++i) {
-            const int j = lane + 64 * i;
-            v[i] = j < cnt ? rowsum[c0 + j] : 0.0;
+        for (int i = 0; i < 8; ++i) {
+            const int64_t idx = c * kGammaChunk + 8 * t + i;
+            e[i] = idx < N ? rowsum[idx] : 0.0;
         }
+        double s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 #pragma unroll
-        for (int i = 0; i < kGammaChunk / 64; ++i) buf[lane + 64 * i] = v[i];
-        __syncthreads();
+        for (int h = 1; h < 64; h *= 2) s += __shfl_down(s, h);
         if (lane == 0)
-            for (int j = 0; j < cnt; ++j) total += buf[j];
+            wsum[wave] = s;
         __syncthreads();
+        double w = lane < kGammaThreads / 64 ? wsum[lane] : 0.0;
+#pragma unroll
+        for (int h = 1; h < kGammaThreads / 64; h *= 2) w += __shfl_down(w, h);
+        __syncthreads();                          // wsum is rewritten by the next chunk
+        if (t == 0) {                             // lane 0 of wave 0 holds the chunk sum
+            double sub = w;
+            for (int64_t k = c; k & 1; k >>= 1) sub = stack[--depth] + sub;
+            stack[depth++] = sub;
+        }
     }
-    if (lane == 0)   // mean of an empty tensor: gamma = 0
+    if (t == 0) {
+        double total = 0.0;
+        if (depth > 0) {
+            total = stack[--depth];
+            while (depth > 0) total = stack[--depth] + total;
+        }
         gamma[0] = (N * K == 0) ? 0.0f : (float)(total / (double)(N * K));
+    }
 }
 
 // Ternarise and pack: one output byte (four weights) per thread.
@@ -206,12 +223,12 @@ __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const void *__re
 hipError_t launch_quant_weight(const float *W, int64_t N, int64_t K, uint8_t *Wp, float *gamma,
                                double *rowsum, hipStream_t s) {
     if (N == 0 || K == 0) {   // gamma = 0, nothing to pack
-        hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(64), 0, s, rowsum, (int64_t)0, K, gamma);
+        hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(kGammaThreads), 0, s, rowsum, (int64_t)0, K, gamma);
         return hipGetLastError();
     }
-    const unsigned nb_rows = (unsigned)((N + kRowsumRows - 1) / kRowsumRows);
-    hipLaunchKernelGGL(rowsum_abs_kernel, dim3(nb_rows), dim3(64), 0, s, W, N, K, rowsum);
-    hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(64), 0, s, rowsum, N, K, gamma);
+    const unsigned nb_rows = (unsigned)((N + kRowsumWaves - 1) / kRowsumWaves);
+    hipLaunchKernelGGL(rowsum_abs_kernel, dim3(nb_rows), dim3(64 * kRowsumWaves), 0, s, W, N, K, rowsum);
+    hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(kGammaThreads), 0, s, rowsum, N, K, gamma);
     const int64_t bytes = N * (K / 4);
     const unsigned nb = (unsigned)((bytes + 255) / 256);
     hipLaunchKernelGGL(ternarize_pack_kernel, dim3(nb), dim3(256), 0, s, W, N, K, gamma, Wp);

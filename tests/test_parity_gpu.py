@@ -58,12 +58,26 @@ def _guarded(shape, dtype, fill):
 
 # ---------------------------------------------------------------- weights
 @pytest.mark.parametrize("N,K,seed", [(256, 256, 0), (67, 260, 1), (640, 2560, 2),
-                                      (6912, 2560, 3), (2560, 6912, 4), (1, 4, 5)])
+                                      (6912, 2560, 3), (2560, 6912, 4), (1, 4, 5),
+                                      (20000, 64, 6), (16385, 8, 7)])
 def test_quant_weight_bit_exact(gpu, N, K, seed):
+    """N > 8192 spans several chunks of the row-sum tree."""
     W = workloads.weight(workloads.generator(seed), N, K)
     Wp, g = _gpu_weight(gpu, W)
     Wp_ref, g_ref = oracle.quantize_weight(W.numpy())
     assert _f32_bits(g.cpu().numpy()[0]) == _f32_bits(g_ref)
+    assert np.array_equal(Wp.cpu().numpy(), Wp_ref)
+
+
+@pytest.mark.parametrize("N,K", [(300, 1028), (9000, 12)])
+def test_quant_weight_wide_range_bit_exact(gpu, N, K):
+    """Magnitudes over 9 decades make the fp64 sum depend on its order: gamma
+    must still match the oracle's bits."""
+    g = workloads.generator(800 + N)
+    W = workloads.weight(g, N, K) * torch.pow(10.0, torch.randint(-6, 3, (N, K), generator=g).float())
+    Wp, gam = _gpu_weight(gpu, W)
+    Wp_ref, g_ref = oracle.quantize_weight(W.numpy())
+    assert _f32_bits(gam.cpu().numpy()[0]) == _f32_bits(g_ref)
     assert np.array_equal(Wp.cpu().numpy(), Wp_ref)
 
 
