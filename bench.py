@@ -20,8 +20,10 @@ cold weights, per launch), the prefill GEMM
 FFN tail (gate/up, ReLU² + subln + requant, down), one decode token through
 the full 30-layer linear stack (bitlinear_decode_stack: 521 MB of packed
 weights per token, tokens/s and GB/s), the QAT backward (dX and dW at
-M = 2048 for the FFN shapes) and the CPU oracle on a bounded sample of the
-decode step.
+M = 2048 for the FFN shapes, the absmean quantiser, a whole training step),
+measured ceilings (a device copy; hipBLASLt's int8 GEMM at the prefill
+shape) with the decode and GEMM figures as fractions of them, and the CPU
+oracle on a bounded sample of the decode step (all threads, then one).
 
 Prints one JSON line.
 """
@@ -441,10 +443,21 @@ def bench_copy(torch, steps):
     return dict(bytes_read=n, bytes_written=n, us=round(us, 2), GBs=round(2 * n / us / 1e3, 1))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, workloads, seconds):
     """The oracle, as it stands, on the decode step's four shapes, repeated
-    for about `seconds` of wall time."""
-    import numpy as np
+    for about `seconds` of wall time: the first half on all the threads its
+    OpenMP loops take, the second half on one thread."""
     import oracle
     probs = []
     for i, s in enumerate(workloads.DECODE_SHAPES):
@@ -452,20 +465,61 @@ def cpu_baseline(torch, workloads, seconds):
         Wp, g = oracle.quantize_weight(W.numpy())
         probs.append((s, Wp, g, workloads.bf16_bits(X)))
     step_bytes = sum(decode_bytes(s.K, s.N) for s, _, _, _ in probs)
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        for s, Wp, g, xb in probs:
-            Xq, d = oracle.quant_act(oracle.bf16_to_f32(xb))
-            oracle.bitlinear(Xq, d, Wp, g, s.K)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def timed(limit):
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            for s, Wp, g, xb in probs:
+                Xq, d = oracle.quant_act(oracle.bf16_to_f32(xb))
+                oracle.bitlinear(Xq, d, Wp, g, s.K)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= limit:
+                return passes, el
+
+    cores = oracle.num_threads()
+    passes, el = timed(seconds / 2)
+    oracle.set_num_threads(1)
+    passes1, el1 = timed(seconds / 2)
+    oracle.set_num_threads(cores)
     return {"value": round(step_bytes * passes / el / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": cores, "kind": "oracle",
+            "value_1_thread": round(step_bytes * passes1 / el1 / 1e9, 3),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"{passes} decode steps (4 shapes, M=1, act quant + add/sub/skip "
-                      f"accumulate + fp64 rescale) in {el:.1f} s, one process"}
+                      f"accumulate + fp64 rescale) in {el:.1f} s on {cores} threads, then "
+                      f"{passes1} in {el1:.1f} s on 1 thread, one process"}
+
+
+def bench_ceilings(torch, workloads):
+    """Measured achievable peaks: a 256 MiB device copy (HBM read + write) and
+    hipBLASLt's int8 GEMM (torch._int_mm, int32 out) at the prefill shape
+    M = 2048, K2560 -> N6912."""
+    copy = bench_copy(torch, 20)
+    p = workloads.PREFILL
+    M, K, N = p["M"], p["K"], p["F"]
+    g = workloads.generator(0)
+    A = torch.randint(-127, 128, (M, K), generator=g, dtype=torch.int8).cuda()
+    B = torch.randint(-1, 2, (K, N), generator=g, dtype=torch.int8).cuda()
+    out = dict(hbm_copy_GBs=copy["GBs"])
+    try:
+        for _ in range(3):
+            torch._int_mm(A, B)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(20):
+            torch._int_mm(A, B)
+        t1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * t0.elapsed_time(t1) / 20
+        out["hipblaslt_int8_gemm_us"] = round(us, 2)
+        out["hipblaslt_int8_gemm_TOPS"] = round(2.0 * M * N * K / us / 1e6, 1)
+    except RuntimeError as e:                     # not every build ships the int8 GEMM
+        out["hipblaslt_int8_gemm_error"] = str(e)[:120]
+    return out
 
 
 def main():
@@ -513,6 +567,15 @@ def main():
         out["copy"] = bench_copy(torch, 10)
     if args.part in ("all", "stack"):
         out["stack"] = bench_stack(bl, torch, workloads, max(20, args.steps // 4), 5)
+    if args.part == "all":
+        ceil = bench_ceilings(torch, workloads)
+        out["ceilings"] = ceil
+        if "roofline" in out and ceil.get("hbm_copy_GBs"):
+            out["roofline"]["frac_of_measured_copy"] = round(
+                out["roofline"]["achieved"] / ceil["hbm_copy_GBs"], 4)
+        if "gemm" in out and ceil.get("hipblaslt_int8_gemm_TOPS"):
+            out["gemm"]["frac_of_hipblaslt"] = round(
+                out["gemm"]["TOPS"] / ceil["hipblaslt_int8_gemm_TOPS"], 4)
     if not args.no_cpu and args.part == "all":
         out["cpu_baseline"] = cpu_baseline(torch, workloads, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -28,12 +28,15 @@ def _load():
         return _lib
     path = os.environ.get("BITLINEAR_ORACLE_LIB")   # mutation tests only
     if not path:
-        if not os.path.exists(_build.LIB):
+        if (not os.path.exists(_build.LIB)
+                or os.path.getmtime(_build.SRC) > os.path.getmtime(_build.LIB)):
             _build.build()
         path = _build.LIB
     lib = ctypes.CDLL(path)
     lib.ob_num_threads.restype = ctypes.c_int
     lib.ob_num_threads.argtypes = []
+    lib.ob_set_num_threads.restype = None
+    lib.ob_set_num_threads.argtypes = [ctypes.c_int]
     lib.ob_absmean_gamma.restype = _f32
     lib.ob_absmean_gamma.argtypes = [_p, _i64, _i64]
     lib.ob_ternarize.restype = None
@@ -73,6 +76,11 @@ def _ptr(a):
 def num_threads():
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().ob_num_threads())
+
+
+def set_num_threads(n):
+    """Threads for the oracle's later parallel loops (CPU timing only)."""
+    _load().ob_set_num_threads(int(n))
 
 
 def absmean_gamma(W):

@@ -46,6 +46,9 @@
 /* Threads the OpenMP loops below use (reported with CPU timings). */
 OB_EXPORT int ob_num_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the threads of later parallel loops (for CPU timings at 1 thread). */
+OB_EXPORT void ob_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* ---------------------------------------------------------------------- */
 /* [RPT] §2 (2) AbsMean 量化:  gamma = (1/n) * sum_i |w_i|.
  *
