@@ -272,23 +272,36 @@ __device__ __forceinline__ void mfma_substep(f32x16 (&acc)[2][4], const Frags &f
 // sub-steps' fragments live, which with fp32 A does not fit two workgroups
 // per CU; both loops add the same products in the same order.
 //
-// Contraction split: unit u of the grid is tile u % T (T tiles) over the
-// c-steps [z split_steps, (z + 1) split_steps) of z = u / T.  With one split
-// it stores s . C to Out; with several it stores its raw partial sum to
-// Out + z split_stride and split_sum_kernel adds them.
+// Work units.  The first `full` units are whole tiles (scaled and stored to
+// Out).  The remaining `tail` tiles -- a last round that would leave most
+// slots idle -- are split into `splits` contraction ranges of split_steps
+// c-steps: unit full + z tail + t takes tile full + t over the c-steps
+// [z split_steps, (z + 1) split_steps) and stores its raw partial tile
+// (kTI x kTJ floats) to part + (z tail + t) kTI kTJ, for split_sum_kernel.
+// Whole tiles are dispatched first, so the split units fill the slots the
+// last whole round frees; each group runs in XCD-chunked order (full is a
+// multiple of 8).
 template <bool kF32A, bool kPipe>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16x2_kernel(
-    const Operands op, int I, int J, int C, int tiles, int tiles_j, int split_steps,
-    size_t split_stride, const float *__restrict__ scale, float *__restrict__ Out, int ldo) {
+    const Operands op, int I, int J, int C, int full, int tail, int tiles_j, int split_steps,
+    float *__restrict__ part, const float *__restrict__ scale, float *__restrict__ Out, int ldo) {
     __shared__ uint32_t lds[2 * kStageDw];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wi = wave >> 1, wj = wave & 1;
-    const int u = xcd_tile(blockIdx.x, gridDim.x);
-    const int z = u / tiles, tile = u - z * tiles;
+    const int total_steps = (C + kBC - 1) / kBC;
+    const int L = blockIdx.x;
+    const bool whole = L < full;
+    int tile, z = 0;
+    if (whole) {
+        tile = xcd_tile(L, full);
+    } else {
+        const int v = xcd_tile(L - full, gridDim.x - full);
+        z = v / tail;
+        tile = full + (v - z * tail);
+    }
     const int i0 = (tile / tiles_j) * kTI, j0 = (tile % tiles_j) * kTJ;
-    const int cb = z * split_steps * kBC;                 // first column of this split
-    const int steps = min(split_steps, (C + kBC - 1) / kBC - z * split_steps);
-    Out += z * split_stride;
+    const int cb = z * split_steps * kBC;                 // first column of this unit
+    const int steps = whole ? total_steps : min(split_steps, total_steps - z * split_steps);
 
     f32x16 acc[2][4];
 #pragma unroll
@@ -335,6 +348,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         }
     }
 
+    if (!whole) {                                         // raw partial, tile layout
+        float *P = part + (size_t)(z * tail + (tile - full)) * (kTI * kTJ);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int il = wi * 64 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) P[il * kTJ + wj * 128 + b * 32 + (lane & 31)] = acc[a][b][r];
+            }
+        return;
+    }
     const float sc = scale ? scalar_load(scale) : 1.0f;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -352,17 +377,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 
 constexpr int kCUs = 256;
 
-// Adds the partial sums of the contraction splits in split order, then
-// scales: Out[e] = s . (((P0[e] + P1[e]) + P2[e]) + ...), 4 elements a lane.
-__global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ P, int splits,
-                                                        size_t stride, size_t n4,
+// Adds a split tile's partial sums in split order, then scales:
+// Out = s . (((P0 + P1) + P2) + ...).  Block (t, y): tail tile t, rows
+// 16 y .. 16 y + 15; each thread 4 float4 of partials, scalar output stores.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ part, int splits,
+                                                        int full, int tail, int tiles_j, int I, int J,
                                                         const float *__restrict__ scale,
-                                                        float *__restrict__ Out) {
+                                                        float *__restrict__ Out, int ldo) {
     const float sc = scale ? scalar_load(scale) : 1.0f;
-    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n4; e += (size_t)gridDim.x * 256) {
-        float4 a = reinterpret_cast<const float4 *>(P)[e];
+    const int tt = blockIdx.x, tile = full + tt;
+    const int i0 = (tile / tiles_j) * kTI, j0 = (tile % tiles_j) * kTJ;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int e = threadIdx.x + 256 * p;
+        const int row = 16 * blockIdx.y + (e >> 6), col = 4 * (e & 63);
+        const size_t off = (size_t)row * kTJ + col;
+        float4 a = *reinterpret_cast<const float4 *>(part + (size_t)tt * (kTI * kTJ) + off);
         for (int z = 1; z < splits; ++z) {
-            const float4 b = reinterpret_cast<const float4 *>(P + z * stride)[e];
+            const float4 b =
+                *reinterpret_cast<const float4 *>(part + (size_t)(z * tail + tt) * (kTI * kTJ) + off);
             a.x += b.x;
             a.y += b.y;
             a.z += b.z;
@@ -374,49 +407,54 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict_
             a.z = __fmul_rn(a.z, sc);
             a.w = __fmul_rn(a.w, sc);
         }
-        reinterpret_cast<float4 *>(Out)[e] = a;
+        const int i = i0 + row, j = j0 + col;             // J % 64 == 0: 4 columns in or out
+        if (i < I && j < J) {
+            float *o = Out + (size_t)i * ldo + j;
+            o[0] = a.x;
+            o[1] = a.y;
+            o[2] = a.z;
+            o[3] = a.w;
+        }
     }
 }
 
-// Contraction splits of an I x J x C product: while the tiles leave CUs idle
-// (at most one per CU), up to 4 splits of at least 8 c-steps each, aiming at
-// two units per CU.  The same rule sizes the workspace.
-struct Split {
-    int splits, split_steps;
+// Schedule of an I x J x C product over the 2 x 256 workgroup slots (two
+// per CU): whole rounds of tiles run unsplit; a last round that would fill at
+// most half the slots is split along the contraction, up to 8 ways of at
+// least 8 c-steps each.  The same rule sizes the workspace.
+constexpr int kSlots = 2 * kCUs;
+struct Plan {
+    int full, tail, splits, split_steps;
 };
-Split choose_split(int64_t I, int64_t J, int64_t C) {
+Plan plan_product(int64_t I, int64_t J, int64_t C) {
     const int64_t tiles = ((I + kTI - 1) / kTI) * ((J + kTJ - 1) / kTJ);
     const int64_t steps = (C + kBC - 1) / kBC;
-    if (steps == 0)
-        return Split{1, 0};
+    const int64_t full = tiles / kSlots * kSlots, tail = tiles - full;
     int64_t s = 1;
-    if (tiles <= kCUs && steps >= 16)
-        s = std::max<int64_t>(1, std::min<int64_t>({4, 2 * kCUs / tiles, steps / 8}));
+    if (tail > 0 && tail <= kSlots / 2 && steps >= 16)
+        s = std::max<int64_t>(1, std::min<int64_t>({8, kSlots / tail, steps / 8}));
+    if (s == 1)
+        return Plan{(int)tiles, 0, 1, (int)steps};
     const int64_t per = (steps + s - 1) / s;
-    return Split{(int)((steps + per - 1) / per), (int)per};
+    return Plan{(int)full, (int)tail, (int)((steps + per - 1) / per), (int)per};
 }
 
 // fp32 A: the plain loop; bf16 planes: the pipelined loop.  `part` holds
-// splits x I x ldo floats when the product is split.
+// splits x tail x kTI x kTJ floats when the tail is split.
 template <bool kF32A>
 hipError_t launch_product(const Operands &op, int I, int J, int C, const float *scale, float *Out,
                           int ldo, float *part, hipStream_t s) {
     const int64_t ti = (I + kTI - 1) / kTI, tj = (J + kTJ - 1) / kTJ;
-    const Split sp = choose_split(I, J, C);
-    if (ti * tj * sp.splits > INT32_MAX)
+    if (ti * tj * 8 > INT32_MAX)
         return hipErrorInvalidConfiguration;      // more units than a 1-D grid holds
-    const dim3 grid((unsigned)(ti * tj * sp.splits)), block(256);
-    float *dst = sp.splits > 1 ? part : Out;
-    const float *sc = sp.splits > 1 ? nullptr : scale;
-    const size_t stride = (size_t)I * ldo;
-    hipLaunchKernelGGL((gemm_bf16x2_kernel<kF32A, !kF32A>), grid, block, 0, s, op, I, J, C,
-                       (int)(ti * tj), (int)tj, sp.split_steps, stride, sc, dst, ldo);
-    if (sp.splits > 1) {
-        const size_t n4 = stride / 4;             // ldo == J, a multiple of 64
-        const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 8 * kCUs);
-        hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), block, 0, s, part, sp.splits, stride, n4,
-                           scale, Out);
-    }
+    const Plan pl = plan_product(I, J, C);
+    const int64_t units = (int64_t)pl.full + (int64_t)pl.tail * pl.splits;
+    const dim3 block(256);
+    hipLaunchKernelGGL((gemm_bf16x2_kernel<kF32A, !kF32A>), dim3((unsigned)units), block, 0, s, op, I,
+                       J, C, pl.full, pl.tail, (int)tj, pl.split_steps, part, scale, Out, ldo);
+    if (pl.tail > 0)
+        hipLaunchKernelGGL(split_sum_kernel, dim3(pl.tail, kTI / 16), block, 0, s, part, pl.splits,
+                           pl.full, pl.tail, (int)tj, I, J, scale, Out, ldo);
     return hipGetLastError();
 }
 
@@ -425,10 +463,10 @@ size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
-// Partial sums of a split product, I x J floats per split (none unsplit).
+// Partial tiles of a product's split tail (none when nothing is split).
 size_t partial_bytes(int64_t I, int64_t J, int64_t C) {
-    const Split sp = choose_split(I, J, C);
-    return sp.splits > 1 ? (size_t)sp.splits * (size_t)I * (size_t)J * 4 : 0;
+    const Plan pl = plan_product(I, J, C);
+    return pl.tail > 0 ? (size_t)pl.splits * (size_t)pl.tail * (kTI * kTJ) * 4 : 0;
 }
 
 size_t backward_input_ws_bytes(int64_t M, int64_t N, int64_t K) {

@@ -226,23 +226,26 @@ def test_backward_validation(lib):
     big = 1 << 40
     fi, fw = lib.bitlinear_backward_input, lib.bitlinear_backward_weight
     # workspace: Wq^T bf16 with rows padded to 64; (dY o d)^T as two bf16
-    # planes + Xq^T bf16; plus fp32 partial sums when the product is split
-    # (at most one 128 x 256 tile per CU and >= 16 c-steps of 32: up to 4
-    # splits of >= 8 steps, aiming at 2 units per CU).
-    # M = 8, K = 6912: 27 tiles, 80 steps -> 4 splits of 20 steps
+    # planes + Xq^T bf16; plus fp32 partial tiles (128 x 256) when the last
+    # round of tiles over the 512 two-per-CU slots is at most half full and
+    # there are >= 16 c-steps of 32: that tail is split up to 8 ways of >= 8
+    # steps, aiming at the 512 slots.
+    tile = 128 * 256 * 4
+    # M = 8, K = 6912: 27 tiles, 80 steps -> 8 splits of 10 steps
     assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_INPUT, 8, 2560, 6912, 0) == \
-        6912 * 2560 * 2 + 4 * 8 * 6912 * 4
+        6912 * 2560 * 2 + 8 * 27 * tile
     # 4 steps: no split
     assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_INPUT, 8, 100, 128, 0) == 128 * 128 * 2
     assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_WEIGHT, 100, 6, 128, 0) == \
         2 * ((6 * 128 * 2 + 255) // 256 * 256) + 128 * 128 * 2
     # the QAT shapes at M = 2048: dX 2560 <- 6912 has 160 tiles, 216 steps -> 3
-    # splits; the others have more tiles than CUs
+    # splits; dX 6912 <- 2560 has 432 tiles, more than half the slots: none;
+    # dW has 540 tiles = 512 + a tail of 28, 64 steps -> 8 splits
     assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_INPUT, 2048, 6912, 2560, 0) == \
-        2560 * 6912 * 2 + 3 * 2048 * 2560 * 4
+        2560 * 6912 * 2 + 3 * 160 * tile
     assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_INPUT, 2048, 2560, 6912, 0) == 6912 * 2560 * 2
     assert lib.bl_workspace_bytes(bl.BL_OP_BACKWARD_WEIGHT, 2048, 6912, 2560, 0) == \
-        2 * 6912 * 2048 * 2 + 2560 * 2048 * 2
+        2 * 6912 * 2048 * 2 + 2560 * 2048 * 2 + 8 * 28 * tile
     for f in (fi, fw):
         assert f(A16, -1, 8, A16, A4, 64, A4, A16, big, None) == SHAPE
         assert f(A16, 2, 8, A16, A4, 96, A4, A16, big, None) == SHAPE           # K % 64
