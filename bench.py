@@ -223,8 +223,27 @@ def bench_gemm(bl, torch, workloads, steps, warmup):
     us = 1000.0 * t0.elapsed_time(t1) / steps
     ops = 2.0 * M * N * K
     tops = ops / us / 1e6
-    return dict(M=M, K=K, N=N, us=round(us, 2), TOPS=round(tops, 1),
-                frac=round(tops / I8_MFMA_PEAK_TOPS, 4))
+    out = dict(M=M, K=K, N=N, us=round(us, 2), TOPS=round(tops, 1),
+               frac=round(tops / I8_MFMA_PEAK_TOPS, 4))
+    # the prefill down-projection shape, K6912 -> N2560
+    K2, N2 = p["F"], p["N"]
+    W2, X2 = workloads.bitlinear_problem(p["seed"] + 1, M, K2, N2)
+    Wp2, g2 = bl.quant_weight_absmean_pack(W2.cuda())
+    Xq2, d2 = bl.quant_act_absmax_i8(X2.cuda())
+    Y2 = torch.empty((M, N2), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        bl.bitlinear_gemm(Xq2, d2, Wp2, g2, Y=Y2)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        bl.bitlinear_gemm(Xq2, d2, Wp2, g2, Y=Y2)
+    t1.record()
+    torch.cuda.synchronize()
+    us2 = 1000.0 * t0.elapsed_time(t1) / steps
+    t2 = 2.0 * M * N2 * K2 / us2 / 1e6
+    out["down_shape"] = dict(M=M, K=K2, N=N2, us=round(us2, 2), TOPS=round(t2, 1),
+                             frac=round(t2 / I8_MFMA_PEAK_TOPS, 4))
+    return out
 
 
 def bench_ffn(bl, torch, workloads, steps, warmup):
