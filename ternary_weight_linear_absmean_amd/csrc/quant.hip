@@ -181,6 +181,66 @@ __device__ __forceinline__ float block_max(float v, float *red) {
     return r;
 }
 
+// One pass for rows of at most 8192 elements, K % 8 == 0: thread t holds the
+// 8-element groups t, t + 256, ... of its row in registers (all loads in
+// flight at once: 16 bytes per load for bf16, 2 x 16 for fp32), so X is
+// read once; the codes go out as 8-byte words.  Same arithmetic as below.
+constexpr int kActGroups = 4;                     // groups per thread: K <= 8192
+
+template <int DT>
+__global__ __launch_bounds__(kActThreads) void quant_act_row_kernel(const void *__restrict__ X,
+                                                                    int64_t K,
+                                                                    int8_t *__restrict__ Xq,
+                                                                    float *__restrict__ d) {
+    __shared__ float red[kActThreads / 64];
+    const int64_t m = blockIdx.x;
+    const int groups = (int)(K / 8);
+    float x[kActGroups][8];
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kActGroups; ++i) {
+        const int g = threadIdx.x + kActThreads * i;
+        const int gc = min(g, groups - 1);            // a valid address; unused when g >= groups
+        if constexpr (DT == 0) {
+            const float4 *src = reinterpret_cast<const float4 *>(X) + ((size_t)m * K + 8 * gc) / 4;
+            const float4 v0 = src[0], v1 = src[1];
+            x[i][0] = v0.x; x[i][1] = v0.y; x[i][2] = v0.z; x[i][3] = v0.w;
+            x[i][4] = v1.x; x[i][5] = v1.y; x[i][6] = v1.z; x[i][7] = v1.w;
+        } else {
+            const uint4 b = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(X) +
+                                                           (size_t)m * K + 8 * gc);
+            const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x[i][2 * t] = __uint_as_float(w[t] << 16);
+                x[i][2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+            }
+        }
+        if (g < groups) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[i][e]));
+        }
+    }
+    a = block_max(a, red);
+    const float s = act_inv_scale(a);
+#pragma unroll
+    for (int i = 0; i < kActGroups; ++i) {
+        const int g = threadIdx.x + kActThreads * i;
+        if (g < groups) {
+            uint32_t q[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                q[h] = (uint32_t)(act_code(x[i][4 * h], s) & 0xFF) |
+                       ((uint32_t)(act_code(x[i][4 * h + 1], s) & 0xFF) << 8) |
+                       ((uint32_t)(act_code(x[i][4 * h + 2], s) & 0xFF) << 16) |
+                       ((uint32_t)(act_code(x[i][4 * h + 3], s) & 0xFF) << 24);
+            *reinterpret_cast<uint2 *>(Xq + (size_t)m * K + 8 * g) = make_uint2(q[0], q[1]);
+        }
+    }
+    if (threadIdx.x == 0)
+        d[m] = act_scale(a);
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const void *__restrict__ X,
                                                                 int64_t K,
@@ -241,6 +301,11 @@ hipError_t launch_quant_act(const void *X, int dtype, int64_t M, int64_t K, int8
         return hipSuccess;
     const bool vec = (K % 4) == 0;
     const dim3 grid((unsigned)M), block(kActThreads);
+    if (K > 0 && K % 8 == 0 && K <= 8 * kActThreads * kActGroups) {
+        if (dtype == 0) hipLaunchKernelGGL(quant_act_row_kernel<0>, grid, block, 0, s, X, K, Xq, d);
+        else            hipLaunchKernelGGL(quant_act_row_kernel<1>, grid, block, 0, s, X, K, Xq, d);
+        return hipGetLastError();
+    }
     if (dtype == 0) {
         if (vec) hipLaunchKernelGGL((quant_act_kernel<0, true>), grid, block, 0, s, X, K, Xq, d);
         else     hipLaunchKernelGGL((quant_act_kernel<0, false>), grid, block, 0, s, X, K, Xq, d);

@@ -114,7 +114,9 @@ def test_quant_weight_empty(gpu):
 @pytest.mark.parametrize("M,K,dtype,seed", [
     (4, 256, torch.float32, 0), (1, 2560, torch.bfloat16, 1), (1, 6912, torch.bfloat16, 2),
     (64, 6912, torch.bfloat16, 3), (2048, 2560, torch.bfloat16, 4), (3, 257, torch.float32, 5),
-    (5, 260, torch.bfloat16, 6), (2, 1, torch.float32, 7)])
+    (5, 260, torch.bfloat16, 6), (2, 1, torch.float32, 7),
+    (3, 8192, torch.bfloat16, 8), (2, 8200, torch.float32, 9), (7, 6912, torch.float32, 10),
+    (3, 8, torch.bfloat16, 11)])
 def test_quant_act_bit_exact(gpu, M, K, dtype, seed):
     X = workloads.activations(workloads.generator(seed), M, K, dtype=dtype)
     if M > 1:
