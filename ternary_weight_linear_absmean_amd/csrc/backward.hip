@@ -80,16 +80,17 @@ __global__ __launch_bounds__(256) void unpack_transpose_kernel(const uint8_t *__
 }
 
 // (dY o d)^T split into bf16 planes GH, GL [N][ld]: G^T[n][m] = fl(dY[m][n] d[m]),
-// GH = bf16(G^T), GL = bf16(G^T - GH); columns m >= M are zeros.
+// GH = bf16(G^T), GL = bf16(G^T - GH); columns m >= M are zeros.  A 1-D grid
+// of m_tiles x n-tiles 64 x 64 tiles (either count may pass grid.y's limit).
 __global__ __launch_bounds__(256) void transpose_scale_split_kernel(const float *__restrict__ dY,
                                                                     const float *__restrict__ d,
                                                                     int M, int N,
                                                                     uint16_t *__restrict__ GH,
                                                                     uint16_t *__restrict__ GL,
-                                                                    int ld) {
+                                                                    int ld, int m_tiles) {
     __shared__ float s[kTile][kTile + 1];
     const int t = threadIdx.x;
-    const int m0 = blockIdx.x * kTile, n0 = blockIdx.y * kTile;
+    const int m0 = (int)(blockIdx.x % m_tiles) * kTile, n0 = (int)(blockIdx.x / m_tiles) * kTile;
 #pragma unroll
     for (int p = 0; p < kTile * kTile / 256; ++p) {
         const int e = t + 256 * p;
@@ -506,8 +507,11 @@ hipError_t launch_backward_weight(const float *dY, int M, int N, const int8_t *X
     uint16_t *GL = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + plane);
     uint16_t *XT = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + 2 * plane);
     if (mp > 0) {
-        hipLaunchKernelGGL(transpose_scale_split_kernel, dim3(mp / kTile, (N + kTile - 1) / kTile),
-                           dim3(256), 0, s, dY, d, M, N, GH, GL, mp);
+        const int64_t blocks = (int64_t)(mp / kTile) * ((N + kTile - 1) / kTile);
+        if (blocks > INT32_MAX)
+            return hipErrorInvalidConfiguration;  // more tiles than a 1-D grid holds
+        hipLaunchKernelGGL(transpose_scale_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dY, d,
+                           M, N, GH, GL, mp, mp / kTile);
         hipLaunchKernelGGL(transpose_i8_kernel, dim3(mp / kTile, K / kTile), dim3(256), 0, s, Xq, M, K,
                            XT, mp);
     }
