@@ -307,9 +307,10 @@ bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers, const bl_
  * bf16 MFMA with fp32 accumulation.  Each result element is within
  * 1e-3 * sum_c |term_c| of the exact sum (the terms being the products it
  * adds).  Gradients must be finite and below 2^127 in magnitude.  When the
- * output has too few 128 x 256 tiles to fill the GPU, the contraction is
- * split into up to 4 ranges whose fp32 partial sums are added in a fixed
- * order: results are deterministic for given sizes.
+ * last round of 128 x 256 output tiles would leave most of the GPU idle,
+ * those tiles' contraction is split into up to 8 ranges whose fp32 partial
+ * sums are added in a fixed order: results are deterministic for given
+ * sizes.  Calls that share a workspace must not run concurrently.
  * An empty sum (N == 0 for dX, M == 0 for dW) writes zeros and reads no
  * operand (those pointers may then be NULL); an empty output is a no-op.
  * Both are asynchronous on `stream`; errors as for bitlinear_gemm.
@@ -319,11 +320,12 @@ bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers, const bl_
  *   Wp     in   uint8 [N][K/4], 16-byte aligned: the forward's packed weights.
  *   gamma  in   fp32 [1], the forward's weight scale.
  *   M, N, K     0 <= M, N < 2^31 - 63; K % 64 == 0; K <= BL_MAX_K; at most
- *               2^31 - 1 output tiles of 128 x 256 (else BL_ERR_HIP).
+ *               2^28 output tiles of 128 x 256 and 2^31 - 1 transpose tiles
+ *               of 64 x 64 (else BL_ERR_HIP).
  *   dX     out  fp32 [M][K].
  *   ws          >= bl_workspace_bytes(BL_OP_BACKWARD_INPUT, M, N, K, 0) bytes,
  *               16-byte aligned (the weights unpacked to bf16, transposed;
- *               fp32 partial sums when the product is split along N).
+ *               fp32 partial tiles when the product is split along N).
  * bitlinear_backward_weight:
  *   dY     in   fp32 [M][N], 16-byte aligned.
  *   Xq     in   int8 [M][K], 16-byte aligned;  d  in  fp32 [M]: the forward's
@@ -332,7 +334,7 @@ bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers, const bl_
  *   dW     out  fp32 [N][K].
  *   ws          >= bl_workspace_bytes(BL_OP_BACKWARD_WEIGHT, M, N, K, 0) bytes,
  *               16-byte aligned ((dY o d)^T as bf16 hi and lo planes, Xq^T in
- *               bf16; fp32 partial sums when the product is split along M).
+ *               bf16; fp32 partial tiles when the product is split along M).
  * The forward of a training step is quant_weight_absmean_pack on the latent
  * weights, quant_act_absmax_i8 and bitlinear_gemm; the optimiser step is the
  * caller's.
