@@ -137,6 +137,14 @@ def test_python_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         bl.quant_act_absmax_i8(torch.zeros(2, 64))
+    with pytest.raises(TypeError):
+        bl.bitlinear_backward_input(torch.zeros(2, 8), torch.zeros(8, 16, dtype=torch.uint8),
+                                    torch.ones(1))
+    with pytest.raises(TypeError):
+        bl.bitlinear_backward_weight(torch.zeros(2, 8), torch.zeros(2, 64, dtype=torch.int8),
+                                     torch.ones(2))
+    with pytest.raises(TypeError):
+        bl.quant_weight_absmean_pack(torch.zeros(4, 64))
 
 
 def test_fused_validation(lib):
