@@ -97,6 +97,7 @@ def _check_case(gpu, M, K, N, seed, dtype=torch.bfloat16):
     (257, 128, 132),     # M just past two row tiles
     (64, 640, 2560),     # long contraction, 3 tiles: dX split 4 ways
     (200, 2560, 640),    # k/v projection: dX split 2 ways
+    (128, 2560, 2560),   # q/o projection
     (1000, 320, 200),    # many tokens, few tiles: dW split 4 ways
     (4096, 128, 64),     # one dW tile, 128 c-steps: split 8 ways
     (3, 131072, 64),     # the largest K the calls take
