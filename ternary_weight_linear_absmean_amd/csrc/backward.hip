@@ -162,6 +162,26 @@ template <bool kF32A> struct Staged;
 template <> struct Staged<true> { float4 a[4]; uint4 b[4]; };
 template <> struct Staged<false> { uint4 ah[2], al[2]; uint4 b[4]; };
 
+// Row and 16-byte chunk that staged element e of a 16-byte-per-lane operand
+// (A planes, B) takes.  One wave store covers 16 rows of 64 bytes; each
+// 16-lane quarter takes rows {k, k + 4, k + 8, k + 12}, whose 80-byte-pitch
+// bank ranges tile the 64 banks exactly (rows k .. k + 3 would wrap onto
+// each other).  The global load uses the same map, 4 lanes per 64-byte row.
+__device__ __forceinline__ void chunk_of(int e, int &r, int &q) {
+    const int l = e & 63;
+    r = ((e >> 6) << 4) + (l >> 4) + 4 * ((l >> 2) & 3);
+    q = l & 3;
+}
+
+// The same for fp32 A, 8 lanes per 32-float row, each lane storing 8 bytes
+// per plane: a half-wave store covers 4 rows, taken as {k, k + 4, k + 8,
+// k + 12} of a 16-row group that two consecutive 64-lane groups share.
+__device__ __forceinline__ void chunk8_of(int e, int &r, int &q) {
+    const int g = e >> 6, l = e & 63;
+    r = ((g >> 1) << 4) + (((g & 1) << 1) | (l >> 5)) + 4 * ((l >> 3) & 3);
+    q = l & 7;
+}
+
 // Branch-free loads: rows past I (J) read row I - 1 (J - 1), whose products
 // land only in outputs that are never stored; fp32 columns past C read column
 // C - 4, and meet B's zero pad columns.  Planes and B have zero pad columns
@@ -172,16 +192,16 @@ __device__ __forceinline__ void load_stage(Staged<kF32A> &st, const Operands &op
     if constexpr (kF32A) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int e = t + 256 * p;
-            const int r = e >> 3, q = e & 7;              // row i0 + r, columns c0 + 4q .. + 3
+            int r, q;                                     // row i0 + r, columns c0 + 4q .. + 3
+            chunk8_of(t + 256 * p, r, q);
             const int rr = min(i0 + r, I - 1), cc = min(c0 + 4 * q, C - 4);
             st.a[p] = *reinterpret_cast<const float4 *>(op.a32 + (size_t)rr * op.lda + cc);
         }
     } else {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int e = t + 256 * p;
-            const int r = e >> 2, q = e & 3;              // row i0 + r, columns c0 + 8q .. + 7
+            int r, q;                                     // row i0 + r, columns c0 + 8q .. + 7
+            chunk_of(t + 256 * p, r, q);
             const size_t o = (size_t)min(i0 + r, I - 1) * op.lda + c0 + 8 * q;
             const uint4 h = *reinterpret_cast<const uint4 *>(op.ahi + o);
             const uint4 l = *reinterpret_cast<const uint4 *>(op.alo + o);
@@ -191,8 +211,8 @@ __device__ __forceinline__ void load_stage(Staged<kF32A> &st, const Operands &op
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int e = t + 256 * p;
-        const int r = e >> 2, q = e & 3;                  // row j0 + r, columns c0 + 8q .. + 7
+        int r, q;                                         // row j0 + r, columns c0 + 8q .. + 7
+        chunk_of(t + 256 * p, r, q);
         const uint4 v = *reinterpret_cast<const uint4 *>(op.b + (size_t)min(j0 + r, J - 1) * op.ldb +
                                                          c0 + 8 * q);
         st.b[p] = v;
@@ -204,8 +224,8 @@ __device__ __forceinline__ void store_stage(const Staged<kF32A> &st, uint32_t *l
     if constexpr (kF32A) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int e = t + 256 * p;
-            const int r = e >> 3, q = e & 7;
+            int r, q;
+            chunk8_of(t + 256 * p, r, q);
             uint32_t h0, l0, h1, l1;
             split2(st.a[p].x, st.a[p].y, h0, l0);
             split2(st.a[p].z, st.a[p].w, h1, l1);
@@ -215,16 +235,16 @@ __device__ __forceinline__ void store_stage(const Staged<kF32A> &st, uint32_t *l
     } else {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int e = t + 256 * p;
-            const int r = e >> 2, q = e & 3;
+            int r, q;
+            chunk_of(t + 256 * p, r, q);
             *reinterpret_cast<uint4 *>(lds + (kAhiRow + r) * kRowDw + 4 * q) = st.ah[p];
             *reinterpret_cast<uint4 *>(lds + (kAloRow + r) * kRowDw + 4 * q) = st.al[p];
         }
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int e = t + 256 * p;
-        const int r = e >> 2, q = e & 3;
+        int r, q;
+        chunk_of(t + 256 * p, r, q);
         *reinterpret_cast<uint4 *>(lds + (kBRow + r) * kRowDw + 4 * q) = st.b[p];
     }
 }
