@@ -544,7 +544,7 @@ def bench_ceilings(torch, workloads):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import ternary_weight_linear_absmean_amd as bl
