@@ -1,4 +1,5 @@
-// gemv.hip -- W1.58A8 product for a handful of tokens (decode), on the VALU.
+// gemv.hip -- W1.58A8 product for a handful of tokens (decode): v_dot4 on the
+// VALU, and for one token in the fused kernel the int8 MFMA.
 //
 // The product is the add / subtract / skip accumulation of "Microsoft BitNet
 // 深度研究报告", §2 (3) 查找表优化, over the packed 2-bit weights of the
@@ -215,6 +216,13 @@ constexpr int kFThreads = BL_FUSED_THREADS;
 constexpr int kFUnits = 8;
 constexpr int kXPre = 2;            // activation groups per thread loaded ahead of the weights
 
+// Token counts that take the MFMA dot products (the rest use v_dot4).
+#ifndef BL_FUSED_MFMA_MAX_MT
+#define BL_FUSED_MFMA_MAX_MT 1
+#endif
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i as_v4i(uint4 v) { return v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
+
 // 16 consecutive activations as fp32 from their raw 16-byte words: four
 // words of fp32, or two words of bf16 (widening is exact).
 __device__ __forceinline__ void unpack_x16(const uint4 (&raw)[4], int dtype, float (&x)[16]) {
@@ -239,7 +247,20 @@ __device__ __forceinline__ void unpack_x16(const uint4 (&raw)[4], int dtype, flo
     }
 }
 
-template <int MT>
+// kMfma (one token): the dot products run on v_mfma_i32_16x16x64_i8 instead
+// of v_dot4, with the lanes reading the same units as the v_dot4 loop (L
+// lanes per row, lane s of a row on units s, s + L, ...).  Column i of the
+// 16-column B operand is lane i % 16 of a lane group g = lane / 16; with
+// c = L / 4 columns per row, column i belongs to row i / c of the wave and
+// its lane group g holds unit (i % c) + c g of the current slot, so the 4
+// lane groups of the c columns of a row cover the slot's L units.  Row j of
+// the A operand carries, on lane group g, the activations of unit
+// (j % c) + c g: the k layout of A and B then matches wherever j = i (mod c),
+// and D[i % c][i] (accumulator i % c of lane i) is column i's partial sum
+// over its 4 units.  One MFMA does the work of 64 lanes x 4 v_dot4 on the
+// matrix core, beside the other wave's unpacking; the c partials of a row
+// are added with shuffles.
+template <int MT, bool kMfma>
 __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs args) {
     extern __shared__ uint4 xs[];   // [MT][K / 16] transposed code groups, then [MT][K] fp32
     __shared__ float red[kFThreads / 64][MT];
@@ -256,7 +277,19 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     const int r = lane >> lshift;
     const int s = lane & (L - 1);
     const int wg = (int)blockIdx.x - jb.wg_begin;
-    const int row = (wg * (kFThreads / 64) + (tid >> 6)) * (64 >> lshift) + r;
+    const int rows_wg = (kFThreads / 64) * (64 >> lshift);
+    // the lane's row, first unit and unit stride
+    int row, sig, stride;
+    if constexpr (kMfma) {
+        const int c = L >> 2, i = lane & 15;                 // columns per row, column
+        row = wg * rows_wg + (tid >> 6) * (64 >> lshift) + i / c;
+        sig = i % c + c * (lane >> 4);
+        stride = L;
+    } else {
+        row = wg * rows_wg + (tid >> 6) * (64 >> lshift) + r;
+        sig = s;
+        stride = L;
+    }
     const int m0 = blockIdx.y * MT;
     const int mt = min(MT, args.M - m0);
     const int U = K / 64;
@@ -292,7 +325,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     uint4 w[kFUnits];
 #pragma unroll
     for (int q = 0; q < kFUnits; ++q)
-        w[q] = ld_stream(wrow + min(s + q * L, U - 1));   // a job with N == 0 reads its own X here
+        w[q] = ld_stream(wrow + min(sig + q * stride, U - 1));  // a job with N == 0 reads its own X here
 
     // 2. activation quantisation into LDS: keep each group's raw words in LDS
     //    and form max |x| per token; then quantise from LDS.
@@ -374,6 +407,58 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     }
     __syncthreads();
 
+    if constexpr (kMfma) {
+        // 3. dot products on MFMA over the lane's units; slots past the
+        //    row's last unit take zero weights (the loop is wave-uniform)
+        static_assert(MT == 1, "the MFMA mapping carries one token");
+        const int nslot = (U + L - 1) / L;
+        v4i acc4 = v4i{0, 0, 0, 0};
+        for (int i0 = 0; i0 < nslot; i0 += kFUnits) {
+            uint4 wn[kFUnits];
+            const bool more = i0 + kFUnits < nslot;
+            if (more) {
+#pragma unroll
+                for (int q = 0; q < kFUnits; ++q)
+                    wn[q] = ld_stream(wrow + min(sig + (i0 + kFUnits + q) * L, U - 1));
+            }
+#pragma unroll
+            for (int q = 0; q < kFUnits; ++q) {
+                if (i0 + q < nslot) {
+                    const int u = sig + (i0 + q) * L;
+                    const bool ok = u < U;
+                    const int uc = min(u, U - 1);
+                    // selects rather than a branch on the last slot: branches
+                    // keep the compiler from interleaving consecutive units
+                    const uint32_t dws[4] = {ok ? w[q].x : 0u, ok ? w[q].y : 0u, ok ? w[q].z : 0u,
+                                             ok ? w[q].w : 0u};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        uint4 bv;
+                        unpack16(dws[t], bv.x, bv.y, bv.z, bv.w);
+                        acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(xs[4 * uc + t]), as_v4i(bv),
+                                                                     acc4, 0, 0, 0);
+                    }
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int q = 0; q < kFUnits; ++q) w[q] = wn[q];
+            }
+        }
+        // lane i < 16: D[i % c][i], then the sum over the row's c columns
+        const int c = L >> 2;
+        const int j = lane % c;
+        int v = j == 0 ? acc4[0] : j == 1 ? acc4[1] : j == 2 ? acc4[2] : acc4[3];
+        for (int off = c >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        if (lane < 16 && j == 0 && row < N) {
+            float a = red[0][0];
+#pragma unroll
+            for (int vv = 1; vv < kFThreads / 64; ++vv) a = fmaxf(a, red[vv][0]);
+            jb.Y[(size_t)m0 * N + row] = rescale(v, __fmul_rn(gam, act_scale(a)));
+        }
+        return;
+    }
+
     // 3. dot products over this lane's units, software-pipelined
     int acc[MT];
 #pragma unroll
@@ -442,8 +527,8 @@ namespace {
 template <int MT>
 hipError_t launch_fused_mt(const FusedArgs &a, int grid_x, int max_k, int max_es, hipStream_t s) {
     const dim3 grid(grid_x, (a.M + MT - 1) / MT);
-    hipLaunchKernelGGL((gemv_fused_kernel<MT>), grid, dim3(kFThreads), fused_lds_bytes(MT, max_k, max_es),
-                       s, a);
+    hipLaunchKernelGGL((gemv_fused_kernel<MT, (MT <= BL_FUSED_MFMA_MAX_MT)>), grid, dim3(kFThreads),
+                       fused_lds_bytes(MT, max_k, max_es), s, a);
     return hipGetLastError();
 }
 }  // namespace
