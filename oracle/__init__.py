@@ -45,6 +45,12 @@ def _load():
     lib.ob_pack.argtypes = [_p, _i64, _i64, _p]
     lib.ob_unpack.restype = None
     lib.ob_unpack.argtypes = [_p, _i64, _i64, _p]
+    lib.ob_t5_row_bytes.restype = _i64
+    lib.ob_t5_row_bytes.argtypes = [_i64]
+    lib.ob_pack_t5.restype = None
+    lib.ob_pack_t5.argtypes = [_p, _i64, _i64, _p]
+    lib.ob_unpack_t5.restype = None
+    lib.ob_unpack_t5.argtypes = [_p, _i64, _i64, _p]
     lib.ob_bf16_to_f32.restype = None
     lib.ob_bf16_to_f32.argtypes = [_p, _i64, _p]
     lib.ob_quant_act.restype = None
@@ -116,6 +122,40 @@ def unpack(Wp, K):
     out = np.empty((N, K), dtype=np.int8)
     _load().ob_unpack(_ptr(Wp), N, K, _ptr(out))
     return out
+
+
+def t5_row_bytes(K):
+    """Bytes per row of the five-per-byte format (oracle.c, ob_pack_t5)."""
+    return int(_load().ob_t5_row_bytes(int(K)))
+
+
+def pack_t5(Wq):
+    """int8 ternary [N, K] -> five weights per byte, uint8 [N, t5_row_bytes(K)]."""
+    Wq = _c(Wq, np.int8)
+    N, K = Wq.shape
+    out = np.empty((N, t5_row_bytes(K)), dtype=np.uint8)
+    _load().ob_pack_t5(_ptr(Wq), N, K, _ptr(out))
+    return out
+
+
+def unpack_t5(Wt5, K):
+    """uint8 [N, t5_row_bytes(K)] -> int8 ternary [N, K]."""
+    Wt5 = _c(Wt5, np.uint8)
+    N = Wt5.shape[0]
+    if Wt5.shape[1] != t5_row_bytes(K):
+        raise ValueError("row length does not match K")
+    out = np.empty((N, K), dtype=np.int8)
+    _load().ob_unpack_t5(_ptr(Wt5), N, K, _ptr(out))
+    return out
+
+
+def bitlinear_t5(Xq, d, Wt5, gamma, K):
+    """(acc int32 [M, N], Y float64 [M, N]) of the five-per-byte format: the
+    weights decoded, then the same BitLinear product as the 2-bit format."""
+    Wq = unpack_t5(Wt5, K)
+    if K % 4:
+        raise ValueError("K must be a multiple of 4")
+    return bitlinear(Xq, d, pack(Wq), gamma, K)
 
 
 def quantize_weight(W):

@@ -165,6 +165,50 @@ OB_EXPORT void ob_unpack(const uint8_t *Wp, int64_t N, int64_t K, int8_t *Wq)
         }
 }
 
+/* Denser storage, five weights per byte.  The pages give ternary weights
+ * about 1.58 bits each (log2 3; iaiol.com article, "权重映射为三元值"; the
+ * 0.4 GB model of the aigc.izzi.cn news page) while the stored format is 2
+ * bits ([RPT] 实际存储, the int2 I2_S kernel of its 内核类型 table).  Five
+ * base-3 digits fit one byte (3^5 = 243 <= 256): 1.6 bits per weight.  The
+ * pages give no layout; the one taken here:
+ *   - digit d = w + 1 in {0, 1, 2} (linear in w);
+ *   - byte b of a row holds weights 5b .. 5b + 4; with v = sum_j d_j 3^(4-j)
+ *     (weight 5b first, as the most significant digit) the byte stores
+ *     q = ceil(256 v / 243), so that q / 256 approximates v / 243 from above;
+ *   - weights past K read as 0 (digit 1), and a row is padded to a multiple
+ *     of 16 bytes with such bytes.
+ * Decoding: v = floor(243 q / 256) recovers v exactly (243 q / 256 lies in
+ * [v, v + 243/256)); its base-3 digits are the weights plus one. */
+OB_EXPORT int64_t ob_t5_row_bytes(int64_t K) { return ((K + 4) / 5 + 15) / 16 * 16; }
+
+OB_EXPORT void ob_pack_t5(const int8_t *Wq, int64_t N, int64_t K, uint8_t *Wt5)
+{
+    int64_t RB = ob_t5_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < RB; ++b) {
+            int v = 0;
+            for (int j = 0; j < 5; ++j) {
+                int64_t k = 5 * b + j;
+                int digit = k < K ? Wq[n * K + k] + 1 : 1;
+                v = 3 * v + digit;
+            }
+            Wt5[n * RB + b] = (uint8_t)((256 * v + 242) / 243);
+        }
+}
+
+OB_EXPORT void ob_unpack_t5(const uint8_t *Wt5, int64_t N, int64_t K, int8_t *Wq)
+{
+    static const int pow3[5] = {1, 3, 9, 27, 81};
+    int64_t RB = ob_t5_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int q = Wt5[n * RB + k / 5];
+            int v = (243 * q) / 256;
+            int digit = (v / pow3[4 - (int)(k % 5)]) % 3;
+            Wq[n * K + k] = (int8_t)(digit - 1);
+        }
+}
+
 /* bf16 -> fp32 widening: the bf16 bits are the upper half of the fp32 bits,
  * so the conversion is exact. */
 OB_EXPORT void ob_bf16_to_f32(const uint16_t *src, int64_t count, float *dst)

@@ -34,6 +34,11 @@ MUTANTS = [
     ("bit_order_msb_first", "<< (2 * j));", "<< (2 * (3 - j)));"),
     ("decode_swapped", "if (code == 1) return 1;\n    if (code == 2) return -1;",
      "if (code == 2) return 1;\n    if (code == 1) return -1;"),
+    ("t5_floor_encoding", "(256 * v + 242) / 243", "(256 * v) / 243"),
+    ("t5_pad_digit_zero", "k < K ? Wq[n * K + k] + 1 : 1;", "k < K ? Wq[n * K + k] + 1 : 0;"),
+    ("t5_digit_order_reversed", "pow3[4 - (int)(k % 5)]", "pow3[(int)(k % 5)]"),
+    ("t5_decode_rounds_up", "(243 * q) / 256", "(243 * q + 255) / 256"),
+    ("t5_rows_unpadded", "((K + 4) / 5 + 15) / 16 * 16", "(K + 4) / 5"),
     ("bf16_shift", "(uint32_t)src[i] << 16;", "(uint32_t)src[i] << 15;"),
     ("act_128", "float s = 127.0f / a;", "float s = 128.0f / a;"),
     ("act_trunc", "float r = nearbyintf(p);", "float r = truncf(p);"),

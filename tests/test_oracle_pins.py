@@ -8,6 +8,7 @@ wrong bit order or code) fails at least one of them.
 
 Runs on the CPU only (no GPU marker).
 """
+import itertools
 import json
 import math
 import os
@@ -165,6 +166,79 @@ def test_unpack_every_byte():
         for j in range(4):
             c = (b >> (2 * j)) & 3
             assert Wq[b, j] == {0: 0, 1: 1, 2: -1, 3: 0}[c]
+
+
+# ------------------------------------------------- five weights per byte
+# Pins of the base-3 storage (oracle.c, ob_pack_t5): a bijection on the 243
+# five-weight patterns, ordered with weight 5b as the most significant digit,
+# decoded identically by an independent method (repeated multiplication of
+# the byte, read as a fraction of 256, by 3: the integer part of each product
+# is the next digit), 16-byte rows at 1.6 bits per weight, zero-weight pads.
+
+def _t5_patterns():
+    return [p for p in itertools.product((-1, 0, 1), repeat=5)]
+
+
+def _digits_by_multiplication(q):
+    r, out = q, []
+    for _ in range(5):
+        t = 3 * r
+        out.append(t >> 8)
+        r = t & 255
+    return out
+
+
+def test_t5_every_pattern_is_a_distinct_ordered_byte():
+    pats = _t5_patterns()                         # lexicographic, first weight most significant
+    Wq = np.array(pats, dtype=np.int8)            # [243, 5]
+    Wt5 = oracle.pack_t5(Wq)
+    assert Wt5.shape == (243, 16)
+    q = Wt5[:, 0].astype(int)
+    assert len(set(q.tolist())) == 243            # injective
+    assert np.all(np.diff(q) > 0)                 # order follows the base-3 value
+    assert np.all(Wt5[:, 1:] == Wt5[0, 1])        # pad bytes: five zero weights
+    assert np.array_equal(oracle.unpack_t5(Wt5, 5), Wq)
+    for i, pat in enumerate(pats):
+        assert _digits_by_multiplication(int(q[i])) == [w + 1 for w in pat]
+
+
+def test_t5_every_byte_value_decodes_as_by_multiplication():
+    Wt5 = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    Wq = oracle.unpack_t5(Wt5, 1280)
+    for b in range(256):
+        assert [int(w) + 1 for w in Wq[0, 5 * b:5 * b + 5]] == _digits_by_multiplication(b)
+
+
+def test_t5_row_layout_and_padding():
+    for K in (1, 4, 5, 6, 79, 80, 81, 2560, 6912):
+        rb = oracle.t5_row_bytes(K)
+        assert rb % 16 == 0 and 5 * rb >= K and 5 * rb < K + 80
+    assert oracle.t5_row_bytes(2560) * 8 == 2560 * 8 // 5        # 1.6 bits per weight
+    zero_byte = oracle.pack_t5(np.zeros((1, 5), dtype=np.int8))[0, 0]
+    assert zero_byte == 128                       # v = 11111 base 3 = 121, ceil(256 * 121 / 243)
+    rng = np.random.default_rng(11)
+    for K in (7, 13, 6912):
+        Wq = rng.integers(-1, 2, size=(4, K)).astype(np.int8)
+        Wt5 = oracle.pack_t5(Wq)
+        assert np.array_equal(oracle.unpack_t5(Wt5, K), Wq)
+        # the digits past K are zero weights, in the last partial byte and after
+        wide = oracle.unpack_t5(Wt5, 5 * Wt5.shape[1])
+        assert np.array_equal(wide[:, :K], Wq) and np.all(wide[:, K:] == 0)
+        assert np.all(Wt5[:, (K + 4) // 5:] == 128)
+
+
+def test_t5_product_equals_2bit_product():
+    rng = np.random.default_rng(12)
+    for M, N, K in ((1, 7, 20), (3, 33, 2560), (2, 5, 6912)):
+        Wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        Xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+        d = rng.random(M).astype(np.float32)
+        g = np.float32(0.37)
+        acc2, Y2 = oracle.bitlinear(Xq, d, oracle.pack(Wq), g, K)
+        acc5, Y5 = oracle.bitlinear_t5(Xq, d, oracle.pack_t5(Wq), g, K)
+        assert np.array_equal(acc2, acc5)
+        assert np.array_equal(acc5, Xq.astype(np.int64) @ Wq.astype(np.int64).T)
+        assert np.array_equal(Y2, Y5)
 
 
 # -------------------------------------------------------- activation quant
