@@ -21,6 +21,8 @@ FFN tail (gate/up, ReLU² + subln + requant, down), one decode token through
 the full 30-layer linear stack (bitlinear_decode_stack: 521 MB of packed
 weights per token, tokens/s and GB/s), the QAT backward (dX and dW at
 M = 2048 for the FFN shapes, the absmean quantiser, a whole training step),
+the decode step's products on five-weights-per-byte rows against the 2-bit
+rows (``t5_storage``: four launches each, pre-quantised tokens, cold weights),
 measured ceilings (a device copy; hipBLASLt's int8 GEMM at the prefill
 shape) with the decode and GEMM figures as fractions of them, and the CPU
 oracle on a bounded sample of the decode step (all threads, then one).
@@ -82,7 +84,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--part", default="all",
-                    choices=["all", "decode", "batched", "gemm", "ffn", "stack", "qat", "copy"],
+                    choices=["all", "decode", "batched", "gemm", "ffn", "stack", "qat", "t5",
+                             "copy"],
                     help="restrict the GPU legs (for profiling runs); 'copy' (not in 'all') "
                          "times a plain device copy of 256 MiB, the reference for the "
                          "byte counters")
@@ -443,6 +446,50 @@ def bench_batched(bl, torch, workloads):
     return rows
 
 
+def bench_t5(bl, torch, workloads, steps, warmup):
+    """Five weights per byte against two bits per weight: the decode step's
+    four products at M = 1 from pre-quantised tokens, as four
+    bitlinear_gemv_t5 launches and as four bitlinear_gemv launches (both on
+    v_dot4), weights rotated over copies past the Infinity Cache, replayed
+    from HIP graphs.  GB/s counts each format's own bytes (weights, int8
+    codes, fp32 outputs, scales)."""
+    shapes = workloads.DECODE_SHAPES
+    base = []
+    for i, s in enumerate(shapes):
+        W, X = workloads.bitlinear_problem(i, 1, s.K, s.N)
+        Wp, g = bl.quant_weight_absmean_pack(W.cuda())
+        Xq, d = bl.quant_act_absmax_i8(X.cuda())
+        base.append(dict(shape=s, Wp=Wp, Wt5=bl.bitlinear_repack_t5(Wp), g=g, Xq=Xq, d=d,
+                         Y=torch.empty((1, s.N), dtype=torch.float32, device="cuda")))
+    out = {}
+    for name, key, call in (("2bit", "Wp", bl.bitlinear_gemv), ("t5", "Wt5", bl.bitlinear_gemv_t5)):
+        per_step = sum(p[key].numel() for p in base)
+        reps = STEPS_PER_GRAPH * math.ceil(max(2, math.ceil(COLD_BYTES / per_step)) / STEPS_PER_GRAPH)
+        copies = [[p[key]] + [p[key].clone() for _ in range(reps - 1)] for p in base]
+
+        def step(r):
+            for p, c in zip(base, copies):
+                call(p["Xq"], p["d"], c[r], p["g"], Y=p["Y"])
+        for r in range(reps):
+            step(r)
+        torch.cuda.synchronize()
+        graphs = capture(torch, step, reps, STEPS_PER_GRAPH)
+        ms = replay_ms(torch, graphs, steps, warmup, STEPS_PER_GRAPH)
+        us = 1000.0 * ms / steps
+        nbytes = per_step + sum(p["shape"].K + 4 * p["shape"].N + 8 for p in base)
+        out[name] = dict(us_per_step=round(us, 3), weight_bytes=per_step, step_bytes=nbytes,
+                         GBs=round(nbytes / us / 1e3, 1), launches_per_step=len(base))
+        del copies, graphs
+    Y2 = [p["Y"].clone() for p in base]
+    for p in base:
+        bl.bitlinear_gemv_t5(p["Xq"], p["d"], p["Wt5"], p["g"], Y=p["Y"])
+    torch.cuda.synchronize()
+    out["identical_outputs"] = all(torch.equal(a.view(torch.int32), p["Y"].view(torch.int32))
+                                   for a, p in zip(Y2, base))
+    out["time_ratio_t5_over_2bit"] = round(out["t5"]["us_per_step"] / out["2bit"]["us_per_step"], 3)
+    return out
+
+
 def bench_copy(torch, steps):
     """A plain device-to-device copy of 256 MiB: the kernel whose HBM byte
     counters (FETCH_SIZE, WRITE_SIZE) calibrate the ones read for the GEMV."""
@@ -568,7 +615,7 @@ def main():
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic(),
-                           "kernel": "gemv_fused_kernel<1> (bitlinear_gemv_fused, 4 jobs, M=1)",
+                           "kernel": "gemv_fused_kernel<1, true> (bitlinear_gemv_fused, 4 jobs, M=1)",
                            "avg_launch_us": round(dec["kernel_us"], 3),
                            "bytes_per_launch": dec["step_bytes"]}
         out["decode_unfused"] = dec["unfused"]
@@ -582,6 +629,8 @@ def main():
         out["ffn"] = bench_ffn(bl, torch, workloads, max(5, args.steps // 40), 2)
     if args.part in ("all", "qat"):
         out["qat_backward"] = bench_qat(bl, torch, workloads, max(5, args.steps // 40), 2)
+    if args.part in ("all", "t5"):
+        out["t5_storage"] = bench_t5(bl, torch, workloads, max(20, args.steps // 2), 10)
     if args.part == "copy":
         out["copy"] = bench_copy(torch, 10)
     if args.part in ("all", "stack"):

@@ -293,6 +293,50 @@ bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers, const bl_
                                  void *stream);
 
 /* ------------------------------------------------------------------------
+ * Five ternary weights per byte -- the denser storage the 1.58-bit figure
+ * points to: [NEWS] "权重映射为三元值" (log2 3 = 1.58 bits per weight), the
+ * 0.4 GB model of the aigc.izzi.cn news page "微软发布新型语言模型 BitNet
+ * b1.58 2B4T，占用内存仅0.4GB", against the 2-bit codes of [RPT] 实际存储 and
+ * the int2 I2_S kernel of [RPT] 内核类型.  3^5 = 243 <= 256: 1.6 bits per
+ * weight, 20% fewer bytes than Wp.
+ *
+ * Format Wt5 (the pages give none): uint8 [N][bitlinear_t5_row_bytes(K)],
+ * row-major.  Byte b of row n holds weights k = 5b .. 5b+4 as the base-3
+ * digits d = w + 1 of v = sum_j d_j 3^(4-j) (weight 5b most significant),
+ * stored as q = ceil(256 v / 243); v = floor(243 q / 256) recovers v.
+ * Weights past K read as 0 (digit 1); rows are padded with such bytes to a
+ * multiple of 16 bytes.
+ */
+
+/* Bytes per Wt5 row: ceil(K / 5) rounded up to a multiple of 16; 0 when K is
+ * negative or above BL_MAX_K. */
+size_t bitlinear_t5_row_bytes(int64_t K);
+
+/* bitlinear_repack_t5 -- Wp (2-bit codes) -> Wt5, the same ternary weights.
+ *   Wp     in   uint8 [N][K/4], 16-byte aligned.
+ *   N, K        N >= 0, K >= 0, K % 4 == 0, K <= BL_MAX_K (N*K == 0: no-op).
+ *   Wt5    out  uint8 [N][bitlinear_t5_row_bytes(K)], 16-byte aligned.
+ * Bit-exact (integer arithmetic only).
+ */
+bl_status bitlinear_repack_t5(const uint8_t *Wp, int64_t N, int64_t K, uint8_t *Wt5,
+                              void *stream);
+
+/* bitlinear_gemv_t5 -- bitlinear_gemv on Wt5 rows, M = 1..8 tokens.
+ *   Xq, d, gamma, Y, acc   as bitlinear_gemv (acc optional; Y and acc
+ *                          bit-identical to bitlinear_gemv on the same
+ *                          ternary weights).
+ *   Wt5    in   uint8 [N][bitlinear_t5_row_bytes(K)], 16-byte aligned.
+ *   M           0 <= M <= 8 (M == 0 or N == 0: no-op).
+ *   K           K > 0, K % 4 == 0, K <= BL_MAX_K, and the staged codes of a
+ *               token tile (1, 2, 4 or 8 tokens for M = 1, 2, 3..4, 5..8) at
+ *               80 bytes per 16 Wt5 bytes of a row must fit 64 KiB
+ *               (BL_ERR_SHAPE otherwise; e.g. M = 1 takes K <= 65520).
+ */
+bl_status bitlinear_gemv_t5(const int8_t *Xq, const float *d, int64_t M, const uint8_t *Wt5,
+                            const float *gamma, int64_t N, int64_t K, float *Y, int32_t *acc,
+                            void *stream);
+
+/* ------------------------------------------------------------------------
  * bitlinear_backward_input / bitlinear_backward_weight -- the backward pass
  * of quantisation-aware training through one BitLinear.
  * [RPT] §2 (4) 量化感知训练: the forward uses the quantised weights, the

@@ -10,5 +10,6 @@ from ._native import (  # noqa: F401
     BL_STACK_PERSISTENT, EXPORTS, LAYER_GAMMAS, LAYER_WEIGHTS, LIB_PATH, BitLinearError,
     GemvJob, Layer, StackDims, bitlinear_backward_input, bitlinear_backward_weight,
     bitlinear_decode_stack, bitlinear_ffn_relu2, bitlinear_gemm, bitlinear_gemv,
-    bitlinear_gemv_fused, load, quant_act_absmax_i8, quant_weight_absmean_pack, workspace_bytes,
+    bitlinear_gemv_fused, bitlinear_gemv_t5, bitlinear_repack_t5, load, quant_act_absmax_i8,
+    quant_weight_absmean_pack, t5_row_bytes, workspace_bytes,
 )

@@ -27,6 +27,7 @@ STATUS = {0: "BL_OK", 1: "BL_ERR_NULL", 2: "BL_ERR_SHAPE", 3: "BL_ERR_DTYPE",
 EXPORTS = ["quant_weight_absmean_pack", "quant_act_absmax_i8", "bitlinear_gemv",
            "bitlinear_gemm", "bitlinear_gemv_fused", "bitlinear_ffn_relu2",
            "bitlinear_decode_stack", "bitlinear_backward_input", "bitlinear_backward_weight",
+           "bitlinear_t5_row_bytes", "bitlinear_repack_t5", "bitlinear_gemv_t5",
            "bl_workspace_bytes", "bl_status_string", "bl_last_error", "bl_abi_version"]
 BL_OP_DECODE_STACK = 2
 BL_OP_BACKWARD_INPUT = 3
@@ -103,6 +104,12 @@ def load():
         f.restype = ctypes.c_int
         f.argtypes = [_p, _i64, _i64, _p, _p, _i64, _p, _p, _sz, _p]
     lib.bl_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64]
+    lib.bitlinear_t5_row_bytes.restype = _sz
+    lib.bitlinear_t5_row_bytes.argtypes = [_i64]
+    lib.bitlinear_repack_t5.restype = st
+    lib.bitlinear_repack_t5.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.bitlinear_gemv_t5.restype = st
+    lib.bitlinear_gemv_t5.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _p]
     lib.bl_status_string.restype = ctypes.c_char_p
     lib.bl_status_string.argtypes = [ctypes.c_int]
     lib.bl_last_error.restype = ctypes.c_char_p
@@ -209,6 +216,52 @@ def bitlinear_gemv(Xq, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=No
 def bitlinear_gemm(Xq, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=None):
     """Y [M, N] fp32 for any M on int8 MFMA; with want_acc also int32 acc."""
     return _product("bitlinear_gemm", Xq, d, Wp, gamma, Y, acc, want_acc, stream)
+
+
+def t5_row_bytes(K):
+    """Bytes per row of the five-weights-per-byte format (0 if K is out of range)."""
+    return int(load().bitlinear_t5_row_bytes(K))
+
+
+def bitlinear_repack_t5(Wp, K=None, Wt5=None, stream=None):
+    """2-bit packed Wp [N, K/4] -> Wt5 uint8 [N, t5_row_bytes(K)] (same weights)."""
+    _dev(Wp, torch.uint8, "Wp")
+    N = Wp.shape[0]
+    K = Wp.shape[1] * 4 if K is None else K
+    if Wp.dim() != 2 or Wp.shape[1] * 4 != K:
+        raise ValueError(f"Wp must be [N, K/4], got {tuple(Wp.shape)} for K={K}")
+    rb = t5_row_bytes(K)
+    Wt5 = _dev(Wt5, torch.uint8, "Wt5") if Wt5 is not None else torch.empty(
+        (N, rb), dtype=torch.uint8, device=Wp.device)
+    if tuple(Wt5.shape) != (N, rb):
+        raise ValueError(f"Wt5 must be [{N}, {rb}]")
+    _check("bitlinear_repack_t5", load().bitlinear_repack_t5(_ptr(Wp), N, K, _ptr(Wt5),
+                                                             _stream(stream)))
+    return Wt5
+
+
+def bitlinear_gemv_t5(Xq, d, Wt5, gamma, Y=None, acc=None, want_acc=False, stream=None):
+    """Y [M, N] fp32 from five-per-byte weights, 1 <= M <= 8; with want_acc
+    also the int32 accumulator."""
+    _dev(Xq, torch.int8, "Xq")
+    _dev(d, torch.float32, "d")
+    _dev(Wt5, torch.uint8, "Wt5")
+    _dev(gamma, torch.float32, "gamma")
+    M, K = Xq.shape
+    N = Wt5.shape[0]
+    if Wt5.dim() != 2 or Wt5.shape[1] != t5_row_bytes(K):
+        raise ValueError(f"Wt5 must be [N, {t5_row_bytes(K)}], got {tuple(Wt5.shape)}")
+    if d.shape != (M,):
+        raise ValueError("d must be [M]")
+    Y = _dev(Y, torch.float32, "Y") if Y is not None else torch.empty(
+        (M, N), dtype=torch.float32, device=Xq.device)
+    if acc is None and want_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    _dev(acc, torch.int32, "acc")
+    _check("bitlinear_gemv_t5", load().bitlinear_gemv_t5(
+        _ptr(Xq), _ptr(d), M, _ptr(Wt5), _ptr(gamma), N, K, _ptr(Y), _ptr(acc),
+        _stream(stream)))
+    return (Y, acc) if want_acc or acc is not None else Y
 
 
 def bitlinear_gemv_fused(jobs, stream=None):

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 
 SOURCES = ["api.cpp", "quant.hip", "gemv.hip", "gemm.hip", "gemm_skinny.hip", "ffn.hip",
-           "stack.hip", "stack_persistent.hip", "backward.hip"]
+           "stack.hip", "stack_persistent.hip", "backward.hip", "t5.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -472,3 +472,69 @@ BL_EXPORT bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers,
                                             dims->path, static_cast<hipStream_t>(stream)),
                     name);
 }
+
+BL_EXPORT size_t bitlinear_t5_row_bytes(int64_t K) {
+    if (K < 0 || K > BL_MAX_K)
+        return 0;
+    return (size_t)bl::t5_row_bytes(K);
+}
+
+BL_EXPORT bl_status bitlinear_repack_t5(const uint8_t *Wp, int64_t N, int64_t K, uint8_t *Wt5,
+                                        void *stream) {
+    const char *name = "bitlinear_repack_t5";
+    if (N < 0 || K < 0 || K % 4 != 0 || K > BL_MAX_K || N > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: need N in [0, 2^31), K in [0, %d] with K %% 4 == 0 "
+                    "(N=%lld K=%lld)", name, BL_MAX_K, (long long)N, (long long)K);
+    if (N == 0 || K == 0)
+        return ok();
+    // one thread per 16 output bytes, 256 per workgroup, a 1-D grid
+    const int64_t blocks = (N * (bl::t5_row_bytes(K) / 16) + 255) / 256;
+    if (blocks > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: N=%lld K=%lld needs %lld workgroups (max 2^31-1)", name,
+                    (long long)N, (long long)K, (long long)blocks);
+    if (!Wp || !Wt5)
+        return fail(BL_ERR_NULL, "%s: NULL pointer (Wp=%p Wt5=%p)", name, (const void *)Wp,
+                    (void *)Wt5);
+    if (!aligned(Wp, 16) || !aligned(Wt5, 16))
+        return fail(BL_ERR_ALIGN, "%s: Wp and Wt5 must be 16-byte aligned", name);
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+    return launched(bl::launch_repack_t5(Wp, (int)N, (int)K, Wt5, static_cast<hipStream_t>(stream)),
+                    name);
+}
+
+BL_EXPORT bl_status bitlinear_gemv_t5(const int8_t *Xq, const float *d, int64_t M,
+                                      const uint8_t *Wt5, const float *gamma, int64_t N, int64_t K,
+                                      float *Y, int32_t *acc, void *stream) {
+    const char *name = "bitlinear_gemv_t5";
+    if (M < 0 || N < 0 || K < 0)
+        return fail(BL_ERR_SHAPE, "%s: negative size (M=%lld N=%lld K=%lld)", name, (long long)M,
+                    (long long)N, (long long)K);
+    if (M > bl::kT5MaxTokens)
+        return fail(BL_ERR_SHAPE, "%s: M=%lld exceeds %d", name, (long long)M, bl::kT5MaxTokens);
+    if (N > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: N=%lld exceeds 2^31-1", name, (long long)N);
+    if (K == 0 || K % 4 != 0 || K > BL_MAX_K)
+        return fail(BL_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 4, <= %d", name,
+                    (long long)K, BL_MAX_K);
+    if (M == 0 || N == 0)
+        return ok();
+    if (bl::t5_lds_bytes((int)M, K) > bl::kT5MaxLds)
+        return fail(BL_ERR_SHAPE, "%s: M=%lld K=%lld stages %zu bytes of codes (max %zu)", name,
+                    (long long)M, (long long)K, bl::t5_lds_bytes((int)M, K), bl::kT5MaxLds);
+    if (!Xq || !d || !Wt5 || !gamma || !Y)
+        return fail(BL_ERR_NULL, "%s: NULL pointer (Xq=%p d=%p Wt5=%p gamma=%p Y=%p)", name,
+                    (const void *)Xq, (const void *)d, (const void *)Wt5, (const void *)gamma,
+                    (const void *)Y);
+    if (!aligned(Xq, 16) || !aligned(Wt5, 16))
+        return fail(BL_ERR_ALIGN, "%s: Xq and Wt5 must be 16-byte aligned", name);
+    if (!aligned(d, 4) || !aligned(gamma, 4) || !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+        return fail(BL_ERR_ALIGN, "%s: d, gamma, Y and acc must be 4-byte aligned", name);
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+    return launched(bl::launch_gemv_t5(Xq, d, (int)M, Wt5, gamma, (int)N, (int)K, Y, acc,
+                                       static_cast<hipStream_t>(stream)),
+                    name);
+}

@@ -87,6 +87,23 @@ hipError_t launch_backward_input(const float *dY, int M, int N, const uint8_t *W
 hipError_t launch_backward_weight(const float *dY, int M, int N, const int8_t *Xq, const float *d,
                                   int K, float *dW, void *ws, hipStream_t s);
 
+// Five ternary weights per byte (t5.hip): bytes per row (a multiple of 16),
+// the token tile of the product, and its LDS bytes (the staged codes of a
+// tile: 80 bytes per 16-byte weight unit and token).
+constexpr int64_t t5_row_bytes(int64_t K) { return ((K + 4) / 5 + 15) / 16 * 16; }
+constexpr int kT5MaxTokens = 8;
+constexpr int t5_tile(int M) { return M == 1 ? 1 : M == 2 ? 2 : M <= 4 ? 4 : 8; }
+constexpr size_t t5_lds_bytes(int M, int64_t K) {
+    return (size_t)t5_tile(M) * (size_t)(t5_row_bytes(K) / 16) * 80;
+}
+constexpr size_t kT5MaxLds = 64 * 1024;
+// Wp [N][K/4] (2-bit codes) -> Wt5 [N][t5_row_bytes(K)]; K % 4 == 0.
+hipError_t launch_repack_t5(const uint8_t *Wp, int N, int K, uint8_t *Wt5, hipStream_t s);
+// Y = float(acc) * fl(gamma * d[m]) from the five-per-byte rows; 1 <= M <= 8,
+// K % 4 == 0, K > 0, t5_lds_bytes(M, K) <= kT5MaxLds.
+hipError_t launch_gemv_t5(const int8_t *Xq, const float *d, int M, const uint8_t *Wt5,
+                          const float *gamma, int N, int K, float *Y, int32_t *acc, hipStream_t s);
+
 // Picks the VALU kernel for M <= kGemvMaxTokens and MFMA otherwise.
 hipError_t launch_bitlinear(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                             const float *gamma, int N, int K, float *Y, int32_t *acc,

@@ -92,6 +92,38 @@ def test_product_validation(lib):
     assert lib.bitlinear_gemv(A16, A4, 65, A16, A4, 8, 64, A4, None, None) == SHAPE
 
 
+def test_t5_validation(lib):
+    rb, rp, gv = lib.bitlinear_t5_row_bytes, lib.bitlinear_repack_t5, lib.bitlinear_gemv_t5
+    # rows: ceil(K / 5) bytes rounded up to 16
+    assert [rb(k) for k in (0, 1, 5, 80, 81, 2560, 6912)] == [0, 16, 16, 16, 32, 512, 1392]
+    assert rb(-1) == 0 and rb(2 * bl.BL_MAX_K) == 0
+    # repack
+    assert rp(A16, -1, 64, A16, None) == SHAPE
+    assert rp(A16, 2, 66, A16, None) == SHAPE                            # K % 4
+    assert rp(A16, 2, 2 * bl.BL_MAX_K, A16, None) == SHAPE
+    assert rp(A16, 2 ** 31 - 1, bl.BL_MAX_K, A16, None) == SHAPE         # grid size
+    assert rp(None, 0, 64, None, None) == OK and rp(None, 3, 0, None, None) == OK
+    assert rp(None, 2, 64, A16, None) == NULL
+    assert rp(A16, 2, 64, None, None) == NULL
+    assert rp(A4, 2, 64, A16, None) == ALIGN
+    assert rp(A16, 2, 64, A4, None) == ALIGN
+    # product
+    assert gv(A16, A4, -1, A16, A4, 8, 64, A4, None, None) == SHAPE
+    assert gv(A16, A4, 9, A16, A4, 8, 64, A4, None, None) == SHAPE       # M <= 8
+    assert gv(A16, A4, 1, A16, A4, 8, 66, A4, None, None) == SHAPE       # K % 4
+    assert gv(A16, A4, 1, A16, A4, 8, 0, A4, None, None) == SHAPE        # K > 0
+    assert gv(A16, A4, 1, A16, A4, 8, 65524, A4, None, None) == SHAPE    # staged codes > 64 KiB
+    assert gv(A16, A4, 5, A16, A4, 8, 8164, A4, None, None) == SHAPE
+    assert gv(None, None, 0, None, None, 8, 64, None, None, None) == OK
+    assert gv(None, None, 3, None, None, 0, 64, None, None, None) == OK
+    assert gv(None, A4, 1, A16, A4, 8, 64, A4, None, None) == NULL
+    assert gv(A16, A4, 1, None, A4, 8, 64, A4, None, None) == NULL
+    assert gv(A4, A4, 1, A16, A4, 8, 64, A4, None, None) == ALIGN
+    assert gv(A16, A4, 1, A4, A4, 8, 64, A4, None, None) == ALIGN
+    assert gv(A16, A1, 1, A16, A4, 8, 64, A4, None, None) == ALIGN
+    assert gv(A16, A4, 1, A16, A4, 8, 64, A4, A1, None) == ALIGN
+
+
 def test_quant_validation(lib):
     f = lib.quant_weight_absmean_pack
     assert f(A16, 4, 6, A16, A4, A16, 1 << 20, None) == SHAPE            # K % 4
@@ -145,6 +177,11 @@ def test_python_binding_refuses_cpu_tensors():
                                      torch.ones(2))
     with pytest.raises(TypeError):
         bl.quant_weight_absmean_pack(torch.zeros(4, 64))
+    with pytest.raises(TypeError):
+        bl.bitlinear_repack_t5(torch.zeros(4, 16, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        bl.bitlinear_gemv_t5(torch.zeros(1, 64, dtype=torch.int8), torch.ones(1),
+                             torch.zeros(4, 16, dtype=torch.uint8), torch.ones(1))
 
 
 def test_fused_validation(lib):
