@@ -427,6 +427,15 @@ def test_fused_large_lds(gpu, M, K, dtype):
     _fused_case(gpu, M, [(K, 300)], dtype, 650 + M)
 
 
+@pytest.mark.parametrize("K,N", [(64, 1), (4160, 33), (6208, 130), (8256, 17)])
+def test_fused_one_token_unit_slots(gpu, K, N):
+    """One token runs its dot products on MFMA with the lanes of a row taking
+    units s, s + L, ...: rows of 1 unit, of 65 units (9 slots of 8 lanes: a
+    second batch whose slot is 1/8 valid), 97 units (16 lanes, last slot 1/16
+    valid) and 129 units (16 lanes, 9 slots)."""
+    _fused_case(gpu, 1, [(K, N), (2560, 7)], torch.bfloat16, 660 + K)
+
+
 def test_fused_shared_input_qkv(gpu):
     _fused_case(gpu, 1, [(2560, 2560), (2560, 640), (2560, 640)], torch.bfloat16, 700,
                 share_x=True)
