@@ -297,6 +297,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     static_assert(!GU || (NJ2 == 2 && WN == 4),
                   "gate/up mode: 4 waves across, one gate and one up block each");
     constexpr int AG = BM2 * 8 / kThreads2, BG = BN2 * 2 / kThreads2;
+    // 128 x 256 tiles: a wave raises its priority while it issues its MFMAs
+    // (K6912 -> N2560 at M = 2048: 52.5 against 53.6-54.5 us); the 256 x 256
+    // tiles run slower with it (47.8-48.8 against 43.4-44.2 us).
+    constexpr bool kPrio = MI2 == 2;
     constexpr int kStageA = BM2 * kAPitch, kStageB = BN2 * kBPitch;
     constexpr int BNO = GU ? BN2 / 2 : BN2;    // output columns of a tile
     // LDS: the double-buffered operand stages; in gate/up mode the epilogue
@@ -373,9 +377,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
                 v4i af[MI2];                                                                      \
                 _Pragma("unroll") for (int i = 0; i < MI2; ++i)                                   \
                     af[i] = as_v4i(A[i * 32 * kAPitch + 2 * h]);                                  \
+                if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);                              \
                 _Pragma("unroll") for (int i = 0; i < MI2; ++i)                                   \
                     _Pragma("unroll") for (int j = 0; j < NJ2; ++j)                               \
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0); \
+                if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);                              \
             }                                                                                     \
             if (kt_ + 1 < KT) store_stage2<kThreads2>(NEXT, As + (buf ^ 1) * kStageA, Bs + (buf ^ 1) * kStageB, tid); \
             __syncthreads();                                                                      \
