@@ -25,7 +25,8 @@ the decode step's products on five-weights-per-byte rows against the 2-bit
 rows (``t5_storage``: four launches each, pre-quantised tokens, cold weights),
 measured ceilings (a device copy; hipBLASLt's int8 GEMM at the prefill
 shape) with the decode and GEMM figures as fractions of them, and the CPU
-oracle on a bounded sample of the decode step (all threads, then one).
+oracle on a bounded sample of the decode step (all threads, then one) and
+of the prefill GEMM (32 of its 2048 token rows).
 
 Prints one JSON line.
 """
@@ -544,12 +545,39 @@ def cpu_baseline(torch, workloads, seconds):
             if el >= limit:
                 return passes, el
 
+    # a bounded sample of the prefill GEMM: 32 of its 2048 token rows
+    p = workloads.PREFILL
+    Mg, Kg, Ng = 32, p["K"], p["F"]
+    Wg, Xg = workloads.bitlinear_problem(p["seed"], Mg, Kg, Ng)
+    Wpg, gg = oracle.quantize_weight(Wg.numpy())
+    Xqg, dg = oracle.quant_act(oracle.bf16_to_f32(workloads.bf16_bits(Xg)))
+    gemm_ops = 2.0 * Mg * Kg * Ng
+
+    def timed_gemm(limit):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.bitlinear(Xqg, dg, Wpg, gg, Kg)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= limit:
+                return reps, el
+
     cores = oracle.num_threads()
     passes, el = timed(seconds / 2)
+    greps, gel = timed_gemm(0.5)
     oracle.set_num_threads(1)
     passes1, el1 = timed(seconds / 2)
+    greps1, gel1 = timed_gemm(1.0)
     oracle.set_num_threads(cores)
+    prefill = {"TOPS": round(gemm_ops * greps / gel / 1e12, 5),
+               "TOPS_1_thread": round(gemm_ops * greps1 / gel1 / 1e12, 5),
+               "sample": f"{Mg} of the {p['M']} token rows of the M={p['M']} K{Kg}->N{Ng} "
+                         f"prefill GEMM ({gemm_ops / 1e9:.2f} G int ops per pass): {greps} "
+                         f"passes in {gel:.1f} s on {cores} threads, {greps1} in {gel1:.1f} s "
+                         f"on 1 thread"}
     return {"value": round(step_bytes * passes / el / 1e9, 3), "unit": "GB/s",
+            "prefill_gemm": prefill,
             "cores": cores, "kind": "oracle",
             "value_1_thread": round(step_bytes * passes1 / el1 / 1e9, 3),
             "nproc": os.cpu_count(), "cpu_model": cpu_model(),
