@@ -113,3 +113,34 @@ def test_gemv_t5_rejects(gpu):
     with pytest.raises(ValueError):                                  # row length
         gpu.bitlinear_gemv_t5(torch.zeros(1, 128, dtype=torch.int8, device="cuda"), d[:1],
                               Wt5, g)
+
+
+def test_gemv_t5_graph_replays_match_eager(gpu):
+    """Repack + product captured in a HIP graph, replayed three times with
+    eager work between the replays: every replay equals the eager result."""
+    W, X = workloads.bitlinear_problem(77, 3, 2560, 640)
+    Wp, g = gpu.quant_weight_absmean_pack(W.cuda())
+    Xq, d = gpu.quant_act_absmax_i8(X.cuda())
+    Wt5 = gpu.bitlinear_repack_t5(Wp)
+    Y_eager = gpu.bitlinear_gemv_t5(Xq, d, Wt5, g)
+    torch.cuda.synchronize()
+    Wt5_g = torch.empty_like(Wt5)
+    Y_g = torch.empty_like(Y_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            gpu.bitlinear_repack_t5(Wp, Wt5=Wt5_g, stream=side)
+            gpu.bitlinear_gemv_t5(Xq, d, Wt5_g, g, Y=Y_g, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        Wt5_g.zero_()
+        Y_g.fill_(float(CANARY))
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Wt5_g, Wt5)
+        assert torch.equal(Y_g.view(torch.int32), Y_eager.view(torch.int32))
+        gpu.bitlinear_gemv_t5(Xq, d, Wt5, g)                 # eager work between replays
+        torch.cuda.synchronize()
