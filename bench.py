@@ -25,8 +25,9 @@ the decode step's products on five-weights-per-byte rows against the 2-bit
 rows (``t5_storage``: four launches each, pre-quantised tokens, cold weights),
 measured ceilings (a device copy; hipBLASLt's int8 GEMM at the prefill
 shape) with the decode and GEMM figures as fractions of them, and the CPU
-oracle on a bounded sample of the decode step (all threads, then one) and
-of the prefill GEMM (32 of its 2048 token rows).
+oracle on bounded samples (all threads, then one) of the decode step, the
+prefill GEMM (32 of its 2048 token rows), batched decode (M = 32,
+K2560->N6912) and the prefill FFN block (8 of its 2048 token rows).
 
 Prints one JSON line.
 """
@@ -553,23 +554,63 @@ def cpu_baseline(torch, workloads, seconds):
     Xqg, dg = oracle.quant_act(oracle.bf16_to_f32(workloads.bf16_bits(Xg)))
     gemm_ops = 2.0 * Mg * Kg * Ng
 
-    def timed_gemm(limit):
+    # batched decode: 32 tokens against K2560 -> N6912
+    sb = workloads.BATCHED_SHAPES[0]
+    Wb, Xb = workloads.bitlinear_problem(70, 32, sb.K, sb.N)
+    Wpb, gb = oracle.quantize_weight(Wb.numpy())
+    Xqb, db = oracle.quant_act(oracle.bf16_to_f32(workloads.bf16_bits(Xb)))
+    batched_ops = 2.0 * 32 * sb.K * sb.N
+    # the prefill FFN block on 8 of its 2048 token rows (gate, up, tail, down)
+    F, Nd = p["F"], p["N"]
+    gf = workloads.generator(p["seed"] + 1)
+    Wgf, Wuf, Wdf = (workloads.weight(gf, F, Kg), workloads.weight(gf, F, Kg),
+                     workloads.weight(gf, Nd, F))
+    Xf = workloads.activations(gf, 8, Kg)
+    (Wpgf, ggf), (Wpuf, guf), (Wpdf, gdf) = (oracle.quantize_weight(w.numpy())
+                                            for w in (Wgf, Wuf, Wdf))
+    Xqf, df = oracle.quant_act(oracle.bf16_to_f32(workloads.bf16_bits(Xf)))
+    ffn_ops = 2.0 * 8 * (2 * Kg * F + F * Nd)
+
+    def timed_call(fn, limit):
         reps = 0
         t0 = time.perf_counter()
         while True:
-            oracle.bitlinear(Xqg, dg, Wpg, gg, Kg)
+            fn()
             reps += 1
             el = time.perf_counter() - t0
             if el >= limit:
                 return reps, el
 
+    def timed_gemm(limit):
+        return timed_call(lambda: oracle.bitlinear(Xqg, dg, Wpg, gg, Kg), limit)
+
+    def batched():
+        oracle.bitlinear(Xqb, db, Wpb, gb, sb.K)
+
+    def ffn():
+        oracle.ffn_relu2(Xqf, df, Wpgf, ggf, Wpuf, guf, None, 1e-5, Wpdf, gdf, Kg, F, Nd)
+
     cores = oracle.num_threads()
     passes, el = timed(seconds / 2)
     greps, gel = timed_gemm(0.5)
+    breps, bel = timed_call(batched, 0.5)
+    freps, fel = timed_call(ffn, 0.5)
     oracle.set_num_threads(1)
     passes1, el1 = timed(seconds / 2)
     greps1, gel1 = timed_gemm(1.0)
+    breps1, bel1 = timed_call(batched, 1.0)
+    freps1, fel1 = timed_call(ffn, 1.0)
     oracle.set_num_threads(cores)
+    batched_row = {"TOPS": round(batched_ops * breps / bel / 1e12, 5),
+                   "TOPS_1_thread": round(batched_ops * breps1 / bel1 / 1e12, 5),
+                   "sample": f"M=32 K{sb.K}->N{sb.N} ({batched_ops / 1e9:.2f} G int ops per pass): "
+                             f"{breps} passes in {bel:.1f} s on {cores} threads, {breps1} in "
+                             f"{bel1:.1f} s on 1 thread"}
+    ffn_row = {"TOPS": round(ffn_ops * freps / fel / 1e12, 5),
+               "TOPS_1_thread": round(ffn_ops * freps1 / fel1 / 1e12, 5),
+               "sample": f"8 of the {p['M']} token rows of the prefill FFN block "
+                         f"({ffn_ops / 1e9:.2f} G int ops per pass): {freps} passes in "
+                         f"{fel:.1f} s on {cores} threads, {freps1} in {fel1:.1f} s on 1 thread"}
     prefill = {"TOPS": round(gemm_ops * greps / gel / 1e12, 5),
                "TOPS_1_thread": round(gemm_ops * greps1 / gel1 / 1e12, 5),
                "sample": f"{Mg} of the {p['M']} token rows of the M={p['M']} K{Kg}->N{Ng} "
@@ -577,7 +618,7 @@ def cpu_baseline(torch, workloads, seconds):
                          f"passes in {gel:.1f} s on {cores} threads, {greps1} in {gel1:.1f} s "
                          f"on 1 thread"}
     return {"value": round(step_bytes * passes / el / 1e9, 3), "unit": "GB/s",
-            "prefill_gemm": prefill,
+            "prefill_gemm": prefill, "batched_decode": batched_row, "prefill_ffn": ffn_row,
             "cores": cores, "kind": "oracle",
             "value_1_thread": round(step_bytes * passes1 / el1 / 1e9, 3),
             "nproc": os.cpu_count(), "cpu_model": cpu_model(),
