@@ -54,50 +54,38 @@ OB_EXPORT void ob_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
  *
  * n runs over every element of the weight tensor, so gamma is one number per
  * BitLinear weight matrix W[N][K] (nn.Linear layout: N outputs, K inputs).
- * The pages give no precision or order for the sum.  Reading taken: the sum
- * is in fp64, in one fixed order that parallel hardware can follow:
- *   - within row n, element k goes to partial (k / 4) mod 64, and each of the
- *     64 partials adds its elements in ascending k;
- *   - the 64 partials are added in consecutive pairs, level by level
- *     (p0 + p1, p2 + p3, ..., then (p0 + p1) + (p2 + p3), ...);
- *   - the N row sums, extended with zeros to a power of two, are added in
- *     consecutive pairs in the same way.
- * Divide by n in fp64; round once to fp32.  Every term is >= 0, so added
- * zeros change nothing and any longer zero extension gives the same bits.
- * A fixed order makes gamma reproducible to the bit.  An empty tensor
- * (n == 0) gets gamma = 0. */
-
-/* Consecutive-pair sum of v[0 .. count), count a power of two; overwrites v. */
-static double pairwise_sum(double *v, int64_t count)
-{
-    for (int64_t h = 1; h < count; h *= 2)
-        for (int64_t i = 0; i + h < count; i += 2 * h)
-            v[i] += v[i + h];
-    return v[0];
-}
-
+ * The pages give no precision or order for the sum.  Reading taken: the terms
+ * |w_i| are taken in the tensor's own row-major order, i = n * K + k, and
+ * summed in fp64 by pairwise summation: neighbours are added in pairs
+ * (|w_0| + |w_1|, |w_2| + |w_3|, ...), then neighbouring pair sums, and so on
+ * until one sum is left; a term or sum with no right neighbour at its level
+ * is carried up unchanged (the same as adding a zero term).  The sum is
+ * divided by n in fp64 and rounded once to fp32.  Every |w| is exact in
+ * fp64, so only the pair additions round; pairwise summation keeps that error
+ * below ~log2(n) * 2^-53 of the sum, so gamma is the fp32 nearest the exact
+ * mean unless the mean lies that close to an fp32 rounding boundary.  An
+ * empty tensor (n == 0) gets gamma = 0. */
 OB_EXPORT float ob_absmean_gamma(const float *W, int64_t N, int64_t K)
 {
+    const int64_t n = N * K;
     if (N <= 0 || K <= 0)
         return 0.0f;
-    int64_t P = 1;
-    while (P < N)
-        P *= 2;
-    double *rows = (double *)calloc((size_t)P, sizeof(double));
-    if (!rows)
+    double *v = (double *)malloc((size_t)n * sizeof(double));
+    if (!v)
         return NAN;
+    for (int64_t i = 0; i < n; ++i)
+        v[i] = fabs((double)W[i]);
+    /* level with stride h: v[i] (i a multiple of 2h) holds the sum of the
+     * terms i .. i+h-1; it absorbs its right neighbour v[i + h] if there is
+     * one. */
+    for (int64_t h = 1; h < n; h *= 2) {
 #pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < N; ++n) {
-        double part[64];
-        for (int l = 0; l < 64; ++l)
-            part[l] = 0.0;
-        for (int64_t k = 0; k < K; ++k)
-            part[(k / 4) % 64] += fabs((double)W[n * K + k]);
-        rows[n] = pairwise_sum(part, 64);
+        for (int64_t i = 0; i < n - h; i += 2 * h)
+            v[i] += v[i + h];
     }
-    const double total = pairwise_sum(rows, P);
-    free(rows);
-    return (float)(total / (double)(N * K));
+    const double total = v[0];
+    free(v);
+    return (float)(total / (double)n);
 }
 
 /* [RPT] §2 (2) AbsMean 量化:  Q(w) = round(clamp(w / gamma, -1, 1)).

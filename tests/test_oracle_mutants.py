@@ -22,12 +22,21 @@ from oracle.build import CFLAGS  # noqa: E402
 
 # (name, original text, replacement) -- each original must occur in oracle.c
 MUTANTS = [
-    ("gamma_drops_abs", "part[(k / 4) % 64] += fabs((double)W[n * K + k]);",
-     "part[(k / 4) % 64] += ((double)W[n * K + k]);"),
+    ("gamma_drops_abs", "v[i] = fabs((double)W[i]);", "v[i] = ((double)W[i]);"),
     ("gamma_pairwise_drops_left", "v[i] += v[i + h];", "v[i] = v[i + h];"),
-    ("gamma_skips_last_row", "for (int64_t n = 0; n < N; ++n) {\n        double part[64];",
-     "for (int64_t n = 0; n < N - 1; ++n) {\n        double part[64];"),
-    ("gamma_wrong_n", "total / (double)(N * K)", "total / (double)(N * K + 1)"),
+    ("gamma_skips_last_term", "v[i] = fabs((double)W[i]);",
+     "v[i] = i + 1 < n ? fabs((double)W[i]) : 0.0;"),
+    ("gamma_sequential_sum", "const double total = v[0];",
+     "double total = 0.0;\n    for (int64_t i = 0; i < n; ++i) total += fabs((double)W[i]);"),
+    ("gamma_rows_first",
+     "    for (int64_t h = 1; h < n; h *= 2) {\n#pragma omp parallel for schedule(static)\n"
+     "        for (int64_t i = 0; i < n - h; i += 2 * h)\n            v[i] += v[i + h];\n    }\n",
+     "    for (int64_t r = 0; r < N; ++r)\n        for (int64_t h = 1; h < K; h *= 2)\n"
+     "            for (int64_t i = 0; i < K - h; i += 2 * h)\n"
+     "                v[r * K + i] += v[r * K + i + h];\n"
+     "    for (int64_t h = 1; h < N; h *= 2)\n        for (int64_t i = 0; i < N - h; i += 2 * h)\n"
+     "            v[i * K] += v[(i + h) * K];\n"),
+    ("gamma_wrong_n", "total / (double)n", "total / (double)(n + 1)"),
     ("round_ties_away", "Wq[i] = (int8_t)nearbyint(t);", "Wq[i] = (int8_t)round(t);"),
     ("no_clamp", "if (t > 1.0) t = 1.0;", ""),
     ("code_minus_one", "if (q == -1) return 2;", "if (q == -1) return 3;"),

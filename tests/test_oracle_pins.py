@@ -112,13 +112,54 @@ def test_ternarize_threshold_form_random():
     assert np.array_equal(Wq, expect)
 
 
-def test_gamma_is_mean_abs_fp64():
-    """gamma equals numpy's fp64 mean |W| rounded once to fp32 (away from
-    rounding boundaries, summation order cannot matter)."""
-    W = workloads.weight(workloads.generator(3), 512, 768).numpy()
-    g = oracle.absmean_gamma(W)
-    ref = np.abs(W.astype(np.float64)).mean()
-    assert abs(float(g) - ref) <= 0.5 * np.spacing(np.float32(ref)) * 1.0001
+def _exact_abs_sum(W):
+    """sum |w| over W exactly, as a Fraction.  Every fp32 |w| is m * 2^e with
+    an integer m < 2^24; the integers of one exponent are added in int64
+    (exact), then the per-exponent sums as rationals."""
+    a = np.abs(np.asarray(W, dtype=np.float32).astype(np.float64)).ravel()
+    m, e = np.frexp(a)
+    mi = np.round(m * 2.0 ** 24).astype(np.int64)
+    ee = (e - 24).astype(np.int64)
+    assert np.array_equal(np.ldexp(mi.astype(np.float64), ee), a)   # decomposition exact
+    total = Fraction(0)
+    for ev in np.unique(ee[mi != 0]):
+        total += Fraction(int(mi[ee == ev].sum())) * Fraction(2) ** int(ev)
+    return total
+
+
+def _nearest_f32(q):
+    """The fp32 nearest the rational q >= 0, ties to the even significand."""
+    if q == 0:
+        return np.float32(0.0)
+    c = np.float32(float(q))
+    cands = [np.nextafter(c, np.float32(0.0)), c, np.nextafter(c, np.float32(np.inf))]
+    return min(cands, key=lambda v: (abs(Fraction(float(v)) - q), int(v.view(np.uint32)) & 1))
+
+
+def _spread_weights(seed, N, K):
+    """Gaussian weights times 10^u, u uniform in [-30, 30] per element."""
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((N, K)) * 0.02 * 10.0 ** rng.uniform(-30, 30, size=(N, K))
+    return W.astype(np.float32)
+
+
+@pytest.mark.parametrize("N,K,seed,spread", [
+    (512, 768, 3, False), (7, 12, 4, False), (333, 260, 5, False), (3, 20, 6, False),
+    (64, 6912, 7, False), (300, 100, 8, True), (5, 2560, 9, True)])
+def test_gamma_is_nearest_fp32_of_exact_mean(N, K, seed, spread):
+    """The pairwise fp64 sum is within ~log2(n) * 2^-53 of the exact sum, far
+    inside half an fp32 ulp: away from an fp32 midpoint gamma must be the fp32
+    nearest the exact rational mean (computed here without any floating-point
+    addition).  The golden cases cover inputs that sit on a midpoint."""
+    W = _spread_weights(seed, N, K) if spread else workloads.weight(
+        workloads.generator(seed), N, K).numpy()
+    q = _exact_abs_sum(W) / (N * K)
+    ref = _nearest_f32(q)
+    lo, hi = np.nextafter(ref, np.float32(0.0)), np.nextafter(ref, np.float32(np.inf))
+    mids = [(Fraction(float(lo)) + Fraction(float(ref))) / 2,
+            (Fraction(float(ref)) + Fraction(float(hi))) / 2]
+    assert min(abs(q - m) for m in mids) > q * Fraction(1, 2 ** 40)   # not a near-midpoint case
+    assert oracle.absmean_gamma(W) == ref
 
 
 def test_gaussian_statistics():
