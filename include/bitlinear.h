@@ -30,8 +30,11 @@
  *   packed weights Wp: uint8 [N][K/4], row-major.  Byte b of row n holds the
  *     weights k = 4b..4b+3; weight 4b+j sits in bits 2j..2j+1; code 0 = 0,
  *     1 = +1, 2 = -1 (code 3 is never written and reads as 0).
- *   gamma: one fp32 per weight tensor, = fp32(fp64 sum |W| / (N*K)), the sum
- *     taken row by row in ascending k and then over rows in ascending n.
+ *   gamma: one fp32 per weight tensor, = fp32(S / (N*K)) with S = sum |W|
+ *     in fp64 over the N*K weights in row-major order, by pairwise summation:
+ *     neighbouring terms are added in pairs, then neighbouring pair sums, and
+ *     so on until one sum is left (a sum with no right neighbour at its level
+ *     is carried up unchanged); the division is in fp64, rounded once.
  *     Wq = sign(w) where 2|w| > gamma, else 0 (round half to even).
  *   Xq: int8 [M][K] row-major, d: fp32 [M].  Per row: a = max|x|,
  *     s = fp32(127 / a), Xq = clamp(rne(fp32(x * s)), -127, 127),
@@ -66,7 +69,7 @@
 extern "C" {
 #endif
 
-#define BL_ABI_VERSION 1
+#define BL_ABI_VERSION 2
 
 typedef enum {
     BL_OK = 0,
@@ -106,8 +109,10 @@ typedef enum {
  *   Wp     out  uint8 [N][K/4], the packed codes (format above).
  *   gamma  out  fp32 [1]; N*K == 0 gives gamma = 0 and writes no Wp byte.
  *   ws          device workspace of >= bl_workspace_bytes(BL_OP_QUANT_WEIGHT,
- *               0, N, K, 0) bytes (N fp64 row sums), 16-byte aligned.
- * gamma is reproducible to the bit (fixed summation order).
+ *               0, N, K, 0) bytes (one fp64 sum per block of 2048 row-major
+ *               weights), 16-byte aligned.
+ *   N*K <= 2^40 (BL_ERR_SHAPE otherwise).
+ * gamma is reproducible to the bit (the fixed pairwise order above).
  */
 bl_status quant_weight_absmean_pack(const float *W, int64_t N, int64_t K,
                                     uint8_t *Wp, float *gamma,
@@ -271,6 +276,9 @@ typedef struct {
     int64_t H, KV, F, D;
     float eps;
     int32_t path;         /* BL_STACK_AUTO, BL_STACK_LAUNCHES or BL_STACK_PERSISTENT */
+    int32_t wait_us;      /* limit of each wait of the persistent path in microseconds;
+                             0 = 1 s (the default); must be >= 0 */
+    int32_t reserved;     /* must be 0 */
 } bl_stack_dims;
 
 /* How bitlinear_decode_stack runs (same results either way):
@@ -283,14 +291,28 @@ typedef struct {
  *                        the previous barrier resolves.  BL_ERR_SHAPE if the
  *                        sizes exceed its per-workgroup limits on the device
  *                        (2B-class sizes fit).  If the grid is not resident
- *                        as a whole (the device shared with other work) a
- *                        barrier gives up after 1 s and x is filled with NaN.
+ *                        as a whole (the device shared with other work), a
+ *                        wait gives up after dims->wait_us (1 s by default):
+ *                        x is then filled with NaN and the call's status
+ *                        word (bitlinear_decode_stack_status) is set.
  *   BL_STACK_AUTO        persistent where it fits, else launches. */
 enum { BL_STACK_AUTO = 0, BL_STACK_LAUNCHES = 1, BL_STACK_PERSISTENT = 2 };
 
 bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers, const bl_stack_dims *dims,
                                  float *x, float *trace, void *ws, size_t ws_bytes,
                                  void *stream);
+
+/* bitlinear_decode_stack_status -- whether the last bitlinear_decode_stack
+ * call with n_layers > 0 on this workspace finished every wait in time.
+ *   ws, ws_bytes, dims   the workspace and the dims of that call.
+ *   status  out  HOST int32: 0 = the call ran to the end (x is valid);
+ *                1 = a wait of the persistent path gave up (x holds NaN).
+ * Reads 4 bytes of the workspace with a blocking device-to-host copy: call it
+ * only once the stack call's work has finished (e.g. after synchronising its
+ * stream).  Allocates nothing; errors as for bitlinear_decode_stack, plus
+ * BL_ERR_NULL for a NULL status and BL_ERR_HIP if the copy fails. */
+bl_status bitlinear_decode_stack_status(const void *ws, size_t ws_bytes,
+                                        const bl_stack_dims *dims, int32_t *status);
 
 /* ------------------------------------------------------------------------
  * Five ternary weights per byte -- the denser storage the 1.58-bit figure

@@ -26,7 +26,8 @@ STATUS = {0: "BL_OK", 1: "BL_ERR_NULL", 2: "BL_ERR_SHAPE", 3: "BL_ERR_DTYPE",
 
 EXPORTS = ["quant_weight_absmean_pack", "quant_act_absmax_i8", "bitlinear_gemv",
            "bitlinear_gemm", "bitlinear_gemv_fused", "bitlinear_ffn_relu2",
-           "bitlinear_decode_stack", "bitlinear_backward_input", "bitlinear_backward_weight",
+           "bitlinear_decode_stack", "bitlinear_decode_stack_status",
+           "bitlinear_backward_input", "bitlinear_backward_weight",
            "bitlinear_t5_row_bytes", "bitlinear_repack_t5", "bitlinear_gemv_t5",
            "bl_workspace_bytes", "bl_status_string", "bl_last_error", "bl_abi_version"]
 BL_OP_DECODE_STACK = 2
@@ -44,7 +45,8 @@ class Layer(ctypes.Structure):
 class StackDims(ctypes.Structure):
     """bl_stack_dims (include/bitlinear.h)."""
     _fields_ = [("H", ctypes.c_int64), ("KV", ctypes.c_int64), ("F", ctypes.c_int64),
-                ("D", ctypes.c_int64), ("eps", ctypes.c_float), ("path", ctypes.c_int32)]
+                ("D", ctypes.c_int64), ("eps", ctypes.c_float), ("path", ctypes.c_int32),
+                ("wait_us", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 BL_STACK_AUTO = 0
@@ -95,6 +97,9 @@ def load():
     lib.bitlinear_decode_stack.restype = st
     lib.bitlinear_decode_stack.argtypes = [ctypes.POINTER(Layer), ctypes.c_int,
                                            ctypes.POINTER(StackDims), _p, _p, _p, _sz, _p]
+    lib.bitlinear_decode_stack_status.restype = st
+    lib.bitlinear_decode_stack_status.argtypes = [_p, _sz, ctypes.POINTER(StackDims),
+                                                  ctypes.POINTER(ctypes.c_int32)]
     lib.bitlinear_ffn_relu2.restype = st
     lib.bitlinear_ffn_relu2.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p,
                                         ctypes.c_float, _p, _p, _i64, _p, _p, _p, _p, _sz, _p]
@@ -348,12 +353,13 @@ def bitlinear_ffn_relu2(Xq, d, Wg, gamma_g, Wu, gamma_u, Wd, gamma_d, norm_w=Non
 
 
 def bitlinear_decode_stack(layers, x, H, KV, F, D, eps=1e-5, trace=False, ws=None, stream=None,
-                           path=BL_STACK_AUTO):
+                           path=BL_STACK_AUTO, wait_us=0):
     """One decode token through len(layers) layers; x fp32 [H] is updated in
     place.  Each layer is a dict with packed weights Wq..Wd (uint8), gammas
     gq..gd (fp32 [1]) and optional ffn_norm (fp32 [F]).  With trace=True
     returns the per-layer trace [n_layers, 5 H + 2 KV] (x_in, q, k, v, o,
-    x_mid, y).  path: BL_STACK_AUTO, BL_STACK_LAUNCHES or BL_STACK_PERSISTENT."""
+    x_mid, y).  path: BL_STACK_AUTO, BL_STACK_LAUNCHES or BL_STACK_PERSISTENT;
+    wait_us: limit of each wait of the persistent path (0 = 1 s)."""
     _dev(x, torch.float32, "x")
     n = len(layers)
     arr = (Layer * max(1, n))()
@@ -366,7 +372,7 @@ def bitlinear_decode_stack(layers, x, H, KV, F, D, eps=1e-5, trace=False, ws=Non
         nw = L.get("ffn_norm")
         vals.append(_dev(nw, torch.float32, "ffn_norm").data_ptr() if nw is not None else None)
         arr[i] = Layer(*vals)
-    dims = StackDims(H, KV, F, D, float(eps), int(path))
+    dims = StackDims(H, KV, F, D, float(eps), int(path), int(wait_us), 0)
     tr = None
     if trace:
         tr = torch.empty((n, 5 * H + 2 * KV), dtype=torch.float32, device=x.device)
@@ -376,6 +382,18 @@ def bitlinear_decode_stack(layers, x, H, KV, F, D, eps=1e-5, trace=False, ws=Non
     _check("bitlinear_decode_stack", load().bitlinear_decode_stack(
         arr, n, ctypes.byref(dims), _ptr(x), _ptr(tr), _ptr(ws), ws.numel(), _stream(stream)))
     return tr
+
+
+def bitlinear_decode_stack_status(ws, H, KV, F, D, path=BL_STACK_AUTO):
+    """Status of the last bitlinear_decode_stack call on workspace ws (uint8
+    device tensor): 0 = it ran to the end, 1 = a wait gave up (x holds NaN).
+    Blocking read; call it once that call's work has finished."""
+    _dev(ws, torch.uint8, "ws")
+    dims = StackDims(H, KV, F, D, 0.0, int(path), 0, 0)
+    out = ctypes.c_int32(-1)
+    _check("bitlinear_decode_stack_status", load().bitlinear_decode_stack_status(
+        _ptr(ws), ws.numel(), ctypes.byref(dims), ctypes.byref(out)))
+    return int(out.value)
 
 
 def bitlinear_backward_input(dY, Wp, gamma, dX=None, ws=None, stream=None):

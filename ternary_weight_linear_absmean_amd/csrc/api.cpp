@@ -147,11 +147,12 @@ BL_EXPORT const char *bl_last_error(void) { return g_last_error; }
 BL_EXPORT int bl_abi_version(void) { return BL_ABI_VERSION; }
 
 BL_EXPORT size_t bl_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t F) {
-    (void)K;
     if (M < 0 || N < 0 || F < 0)
         return 0;
     switch (op) {
-    case BL_OP_QUANT_WEIGHT: return round_up((size_t)N * sizeof(double), 256);
+    case BL_OP_QUANT_WEIGHT:
+        if (K < 0 || K > BL_MAX_K || N > kI32Max) return 0;
+        return round_up((size_t)bl::quant_weight_blocks(N, K) * sizeof(double), 256);
     case BL_OP_FFN_RELU2: return ffn_ws(M, F).total;
     case BL_OP_DECODE_STACK:
         if (N < 0 || K < 0 || F < 0 || N > 16384 || K > 16384 || F > 16384) return 0;
@@ -174,6 +175,8 @@ BL_EXPORT bl_status quant_weight_absmean_pack(const float *W, int64_t N, int64_t
     if (N < 0 || K < 0 || K % 4 != 0 || K > BL_MAX_K || N > kI32Max)
         return fail(BL_ERR_SHAPE, "%s: need N in [0, 2^31), K in [0, %d] with K %% 4 == 0 "
                     "(N=%lld K=%lld)", name, BL_MAX_K, (long long)N, (long long)K);
+    if (N * K > ((int64_t)1 << 40))   // keeps every grid of the three kernels below 2^31
+        return fail(BL_ERR_SHAPE, "%s: N*K=%lld exceeds 2^40 weights", name, (long long)(N * K));
     if (!gamma)
         return fail(BL_ERR_NULL, "%s: gamma is NULL", name);
     if (!aligned(gamma, 4))
@@ -419,21 +422,32 @@ BL_EXPORT bl_status bitlinear_ffn_relu2(const int8_t *Xq, const float *d, int64_
     return launched(e, name);
 }
 
+// Checks of bl_stack_dims shared by the stack call and its status call.
+static bl_status check_stack_dims(const char *name, const bl_stack_dims *dims) {
+    if (!dims)
+        return fail(BL_ERR_NULL, "%s: dims is NULL", name);
+    const int64_t H = dims->H, KV = dims->KV, F = dims->F, D = dims->D;
+    if (H <= 0 || KV <= 0 || F <= 0 || D <= 0 || H % 64 || KV % 64 ||
+        F % 64 || H > 16384 || KV > 16384 || F > 16384 || H % D || KV % D ||
+        (H / D) % (KV / D) || dims->path < BL_STACK_AUTO || dims->path > BL_STACK_PERSISTENT ||
+        !(dims->eps >= 0.0f) || dims->wait_us < 0 || dims->reserved != 0)
+        return fail(BL_ERR_SHAPE, "%s: need H, KV, F multiples of 64 up to 16384; D dividing "
+                    "H and KV; KV/D dividing H/D; eps >= 0; path 0..2; wait_us >= 0; "
+                    "reserved == 0 (H=%lld KV=%lld F=%lld D=%lld)", name, (long long)H,
+                    (long long)KV, (long long)F, (long long)D);
+    return BL_OK;
+}
+
 BL_EXPORT bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers,
                                            const bl_stack_dims *dims, float *x, float *trace,
                                            void *ws, size_t ws_bytes, void *stream) {
     const char *name = "bitlinear_decode_stack";
-    if (!dims)
-        return fail(BL_ERR_NULL, "%s: dims is NULL", name);
+    bl_status st0 = check_stack_dims(name, dims);
+    if (st0 != BL_OK)
+        return st0;
     const int64_t H = dims->H, KV = dims->KV, F = dims->F, D = dims->D;
-    if (n_layers < 0 || H <= 0 || KV <= 0 || F <= 0 || D <= 0 || H % 64 || KV % 64 ||
-        F % 64 || H > 16384 || KV > 16384 || F > 16384 || H % D || KV % D ||
-        (H / D) % (KV / D) || dims->path < BL_STACK_AUTO || dims->path > BL_STACK_PERSISTENT ||
-        !(dims->eps >= 0.0f))
-        return fail(BL_ERR_SHAPE, "%s: need n_layers >= 0; H, KV, F multiples of 64 up to "
-                    "16384; D dividing H and KV; KV/D dividing H/D; eps >= 0; path 0..2 (H=%lld KV=%lld "
-                    "F=%lld D=%lld)", name, (long long)H, (long long)KV, (long long)F,
-                    (long long)D);
+    if (n_layers < 0)
+        return fail(BL_ERR_SHAPE, "%s: n_layers=%d must be >= 0", name, n_layers);
     if (n_layers == 0)
         return ok();
     if (!layers || !x)
@@ -468,9 +482,40 @@ BL_EXPORT bl_status bitlinear_decode_stack(const bl_layer *layers, int n_layers,
                     "per-workgroup limits on this device", name, (long long)H, (long long)KV,
                     (long long)F);
     return launched(bl::launch_decode_stack(layers, n_layers, (int)H, (int)KV, (int)F, (int)D,
-                                            dims->eps, x, trace, static_cast<float *>(ws),
-                                            dims->path, static_cast<hipStream_t>(stream)),
+                                            dims->eps, dims->wait_us, x, trace,
+                                            static_cast<float *>(ws), dims->path,
+                                            static_cast<hipStream_t>(stream)),
                     name);
+}
+
+BL_EXPORT bl_status bitlinear_decode_stack_status(const void *ws, size_t ws_bytes,
+                                                  const bl_stack_dims *dims, int32_t *status) {
+    const char *name = "bitlinear_decode_stack_status";
+    bl_status st = check_stack_dims(name, dims);
+    if (st != BL_OK)
+        return st;
+    if (!status)
+        return fail(BL_ERR_NULL, "%s: status is NULL", name);
+    const size_t need = bl_workspace_bytes(BL_OP_DECODE_STACK, 1, dims->H, dims->KV, dims->F);
+    if (!ws || ws_bytes < need)
+        return fail(BL_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", name, ws_bytes,
+                    ws, need);
+    if (!aligned(ws, 16))
+        return fail(BL_ERR_ALIGN, "%s: ws must be 16-byte aligned", name);
+    st = check_arch();
+    if (st != BL_OK)
+        return st;
+    const bl::StackWs w = bl::stack_ws(static_cast<float *>(const_cast<void *>(ws)), (int)dims->H,
+                                       (int)dims->KV, (int)dims->F);
+    unsigned word = 0;
+    const hipError_t e = hipMemcpy(&word, bl::stack_status_word(w, (int)dims->H, (int)dims->KV,
+                                                                (int)dims->F),
+                                   sizeof word, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail(BL_ERR_HIP, "%s: reading the status word failed: %s", name,
+                    hipGetErrorString(e));
+    *status = word != 0u ? 1 : 0;
+    return ok();
 }
 
 BL_EXPORT size_t bitlinear_t5_row_bytes(int64_t K) {

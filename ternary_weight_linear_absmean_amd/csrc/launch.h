@@ -11,9 +11,11 @@
 
 namespace bl {
 
-// Offline weight path: fp64 row sums of |W| into `rowsum` [N], gamma, packing.
+// Offline weight path: fp64 sums of |W| over blocks of 2048 row-major terms
+// into `bsum` [quant_weight_blocks(N, K)], gamma, packing.
+int64_t quant_weight_blocks(int64_t N, int64_t K);
 hipError_t launch_quant_weight(const float *W, int64_t N, int64_t K, uint8_t *Wp,
-                               float *gamma, double *rowsum, hipStream_t s);
+                               float *gamma, double *bsum, hipStream_t s);
 
 // Per-token absmax int8 quantisation; dtype 0 = fp32, 1 = bf16.
 hipError_t launch_quant_act(const void *X, int dtype, int64_t M, int64_t K,
@@ -130,8 +132,8 @@ enum StackPath { kStackAuto = 0, kStackLaunches = 1, kStackPersistent = 2 };
 // One token (M = 1) through n_layers layers; x [H] fp32 is updated in place.
 // trace: NULL or [n_layers][5 H + 2 KV] = x_in, q, k, v, o, x_mid, y.
 hipError_t launch_decode_stack(const StackLayer *layers, int n_layers, int H, int KV, int F,
-                               int D, float eps, float *x, float *trace, float *ws, int path,
-                               hipStream_t s);
+                               int D, float eps, int wait_us, float *x, float *trace, float *ws,
+                               int path, hipStream_t s);
 
 // The persistent path: one launch per 16 layers, one workgroup per compute
 // unit of the current device.  fits() says whether these sizes fit its
@@ -139,8 +141,12 @@ hipError_t launch_decode_stack(const StackLayer *layers, int n_layers, int H, in
 size_t stack_persistent_ws_floats(int H, int KV, int F);
 bool stack_persistent_fits(int H, int KV, int F, int D);
 hipError_t launch_decode_stack_persistent(const StackLayer *layers, int n_layers, int H, int KV,
-                                          int F, int D, float eps, float *x, float *trace,
-                                          const StackWs &ws, hipStream_t s);
+                                          int F, int D, float eps, int wait_us, float *x,
+                                          float *trace, const StackWs &ws, hipStream_t s);
+// The call's status word in the workspace (0: every wait ended in time), and
+// a launch that clears it.
+unsigned *stack_status_word(const StackWs &ws, int H, int KV, int F);
+hipError_t launch_stack_clear_status(unsigned *err, hipStream_t s);
 
 // FFN tail on fp32 G, U [M][F]: H = relu(G)^2 * U, Hq / dh = absmax int8 of
 // H * g, dz = dh / rms(H).  U == NULL: ungated; norm_w == NULL: unit gain.

@@ -13,77 +13,79 @@ namespace bl {
 namespace {
 
 // ---------------------------------------------------------------------------
-// gamma = (1/n) sum |W| in fp64, in one fixed order (the pages fix none):
-// within a row, element k goes to partial (k / 4) mod 64 and each partial adds
-// its elements in ascending k; the 64 partials are added in consecutive pairs,
-// level by level; the row sums, zero-extended to a power of two, are added in
-// consecutive pairs the same way; then / n in fp64 and one rounding to fp32.
-// Every term is >= 0, so adding +0.0 (tails, padding) changes nothing.
+// gamma = (1/n) sum |W| over the n = N * K terms in the tensor's row-major
+// order, summed in fp64 pairwise (the pages fix no order): neighbours are added
+// in pairs, then neighbouring pair sums, and so on; a sum with no right
+// neighbour at its level is carried up.  Every term is >= 0, so that is the
+// full binary tree over the terms followed by zeros (x + 0 = x), and any
+// aligned run of 2^j terms is one subtree.  Then / n in fp64, one rounding to
+// fp32.
 
-// Row sums, one wave per row: lane l is partial l, reading the float4 units
-// l, l + 64, ... of its row (coalesced, eight units in flight), and the
-// partials are added in consecutive pairs by shuffles (after the step with
-// offset h, lane i * 2h holds the pair sum of its 2h-lane group).
-constexpr int kRowsumWaves = 4;
-constexpr int kRowsumUnroll = 8;
+// Level 1: one wave per block of 2048 consecutive terms (a subtree).  In each
+// 256-term chunk of the block, lane l holds terms 4l .. 4l+3 (one float4) and
+// adds them as (t0 + t1) + (t2 + t3); shuffles then add neighbouring lanes
+// (offset 1, 2, ..., 32: after the step with offset h, lane i * 2h holds the
+// sum of its 2h-lane group).  A lane loads its float4 of all 8 chunks at once
+// (eight 16-byte loads in flight) and lane 0 pairs the 8 chunk sums.  Terms
+// past n read as zeros.
+constexpr int kBlockWaves = 4;
+constexpr int kBlockChunks = 8;
+constexpr int64_t kBlockTerms = 256 * kBlockChunks;
 
-__global__ __launch_bounds__(64 * kRowsumWaves) void rowsum_abs_kernel(const float *__restrict__ W,
-                                                                       int64_t N, int64_t K,
-                                                                       double *__restrict__ rowsum) {
+__global__ __launch_bounds__(64 * kBlockWaves) void blocksum_abs_kernel(const float *__restrict__ W,
+                                                                        int64_t n,
+                                                                        double *__restrict__ bsum) {
     const int lane = threadIdx.x & 63;
-    const int64_t n = (int64_t)blockIdx.x * kRowsumWaves + (threadIdx.x >> 6);
-    if (n >= N)
+    const int64_t b = (int64_t)blockIdx.x * kBlockWaves + (threadIdx.x >> 6);
+    if (b * kBlockTerms >= n)
         return;                                   // whole wave; no barrier follows
-    const float *row = W + n * K;
-    const int64_t units = K / 4;                  // K % 4 == 0
-    double p = 0.0;
-    for (int64_t u0 = lane; u0 < units; u0 += 64 * kRowsumUnroll) {
-        float4 v[kRowsumUnroll];
+    const int64_t units = n / 4;                  // n % 4 == 0
+    const float4 *src = reinterpret_cast<const float4 *>(W);
+    float4 v[kBlockChunks];
 #pragma unroll
-        for (int i = 0; i < kRowsumUnroll; ++i) {
-            const int64_t u = u0 + 64 * i;
-            v[i] = u < units ? *reinterpret_cast<const float4 *>(row + 4 * u)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int i = 0; i < kRowsumUnroll; ++i) {
-            p += fabs((double)v[i].x);
-            p += fabs((double)v[i].y);
-            p += fabs((double)v[i].z);
-            p += fabs((double)v[i].w);
-        }
+    for (int c = 0; c < kBlockChunks; ++c) {
+        const int64_t u = b * (kBlockTerms / 4) + 64 * c + lane;
+        v[c] = u < units ? src[u] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    double s[kBlockChunks];
 #pragma unroll
-    for (int h = 1; h < 64; h *= 2) p += __shfl_down(p, h);
+    for (int c = 0; c < kBlockChunks; ++c)
+        s[c] = (fabs((double)v[c].x) + fabs((double)v[c].y)) +
+               (fabs((double)v[c].z) + fabs((double)v[c].w));
+#pragma unroll
+    for (int h = 1; h < 64; h *= 2) {
+#pragma unroll
+        for (int c = 0; c < kBlockChunks; ++c) s[c] += __shfl_down(s[c], h);
+    }
     if (lane == 0)
-        rowsum[n] = p;
+        bsum[b] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
-// Total: one workgroup of 1024 threads takes the row sums in chunks of 8192
-// (thread t: 8 consecutive values, added in pairs in registers; then lanes by
-// shuffles; then the 16 wave sums in wave 0) -- each chunk sum is a subtree
-// of the zero-extended pair tree.  The chunk sums are combined with a carry
-// stack, as in binary counting: chunk c is pushed, and while the subtree at
-// the top has a left sibling of the same size they are added, left + right.
-// At the end the stack is folded from the top (a missing right sibling is a
-// zero subtree, and x + 0 = x).
+// Upper levels: one workgroup of 1024 threads takes the block sums (the
+// leaves here) in chunks of 8192 (thread t: 8 consecutive leaves, added in
+// pairs in registers; then neighbouring lanes by shuffles; then the 16 wave
+// sums in wave 0) -- each chunk sum is a subtree of the pairwise tree.  The
+// chunk sums are combined with a carry stack, as in binary counting: chunk c
+// is pushed, and while the subtree on top has a left sibling of the same
+// size they are added, left + right.  At the end the stack is folded from the
+// top (a missing right sibling is a zero subtree, and x + 0 = x).
 constexpr int kGammaThreads = 1024;
 constexpr int kGammaChunk = 8 * kGammaThreads;
 
-__global__ __launch_bounds__(kGammaThreads) void gamma_kernel(const double *__restrict__ rowsum,
-                                                              int64_t N, int64_t K,
+__global__ __launch_bounds__(kGammaThreads) void gamma_kernel(const double *__restrict__ leaf,
+                                                              int64_t nleaves, int64_t n,
                                                               float *__restrict__ gamma) {
     __shared__ double wsum[kGammaThreads / 64];
     __shared__ double stack[48];                  // thread 0's carry stack, one entry per level
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     int depth = 0;                                // meaningful in thread 0
-    const int64_t chunks = (N + kGammaChunk - 1) / kGammaChunk;
+    const int64_t chunks = (nleaves + kGammaChunk - 1) / kGammaChunk;
     for (int64_t c = 0; c < chunks; ++c) {
         double e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t idx = c * kGammaChunk + 8 * t + i;
-            e[i] = idx < N ? rowsum[idx] : 0.0;
+            e[i] = idx < nleaves ? leaf[idx] : 0.0;
         }
         double s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 #pragma unroll
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(kGammaThreads) void gamma_kernel(const double *__re
             total = stack[--depth];
             while (depth > 0) total = stack[--depth] + total;
         }
-        gamma[0] = (N * K == 0) ? 0.0f : (float)(total / (double)(N * K));
+        gamma[0] = (n == 0) ? 0.0f : (float)(total / (double)n);
     }
 }
 
@@ -280,18 +282,23 @@ __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const void *__re
 
 }  // namespace
 
+int64_t quant_weight_blocks(int64_t N, int64_t K) { return (N * K + kBlockTerms - 1) / kBlockTerms; }
+
 hipError_t launch_quant_weight(const float *W, int64_t N, int64_t K, uint8_t *Wp, float *gamma,
-                               double *rowsum, hipStream_t s) {
-    if (N == 0 || K == 0) {   // gamma = 0, nothing to pack
-        hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(kGammaThreads), 0, s, rowsum, (int64_t)0, K, gamma);
+                               double *bsum, hipStream_t s) {
+    const int64_t n = N * K;
+    if (n == 0) {   // gamma = 0, nothing to pack
+        hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(kGammaThreads), 0, s, bsum, (int64_t)0,
+                           (int64_t)0, gamma);
         return hipGetLastError();
     }
-    const unsigned nb_rows = (unsigned)((N + kRowsumWaves - 1) / kRowsumWaves);
-    hipLaunchKernelGGL(rowsum_abs_kernel, dim3(nb_rows), dim3(64 * kRowsumWaves), 0, s, W, N, K, rowsum);
-    hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(kGammaThreads), 0, s, rowsum, N, K, gamma);
+    const int64_t nb = quant_weight_blocks(N, K);
+    const unsigned grid_sum = (unsigned)((nb + kBlockWaves - 1) / kBlockWaves);
+    hipLaunchKernelGGL(blocksum_abs_kernel, dim3(grid_sum), dim3(64 * kBlockWaves), 0, s, W, n, bsum);
+    hipLaunchKernelGGL(gamma_kernel, dim3(1), dim3(kGammaThreads), 0, s, bsum, nb, n, gamma);
     const int64_t bytes = N * (K / 4);
-    const unsigned nb = (unsigned)((bytes + 255) / 256);
-    hipLaunchKernelGGL(ternarize_pack_kernel, dim3(nb), dim3(256), 0, s, W, N, K, gamma, Wp);
+    const unsigned nb_pack = (unsigned)((bytes + 255) / 256);
+    hipLaunchKernelGGL(ternarize_pack_kernel, dim3(nb_pack), dim3(256), 0, s, W, N, K, gamma, Wp);
     return hipGetLastError();
 }
 

@@ -71,11 +71,15 @@ StackWs stack_ws(float *ws, int H, int KV, int F) {
 }
 
 hipError_t launch_decode_stack(const StackLayer *layers, int n_layers, int H, int KV, int F,
-                               int D, float eps, float *x, float *trace, float *ws, int path,
-                               hipStream_t s) {
+                               int D, float eps, int wait_us, float *x, float *trace, float *ws,
+                               int path, hipStream_t s) {
     const StackWs w = stack_ws(ws, H, KV, F);
     if (path == kStackPersistent || (path == kStackAuto && stack_persistent_fits(H, KV, F, D)))
-        return launch_decode_stack_persistent(layers, n_layers, H, KV, F, D, eps, x, trace, w, s);
+        return launch_decode_stack_persistent(layers, n_layers, H, KV, F, D, eps, wait_us, x,
+                                              trace, w, s);
+    // this path has no bounded waits: its status is always 0
+    hipError_t e0 = launch_stack_clear_status(stack_status_word(w, H, KV, F), s);
+    if (e0 != hipSuccess) return e0;
     float *q = w.q, *a = w.a, *o = w.o, *y = w.y, *k = w.k, *v = w.v, *G = w.G, *U = w.U;
     float *dh = w.dh, *dz = w.dz;
     int8_t *Hq = w.Hq;

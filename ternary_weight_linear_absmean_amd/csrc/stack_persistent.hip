@@ -37,9 +37,11 @@
 // their dot products are done, and those stream from HBM while the receivers
 // wait for the next input.
 //
-// Every wait is bounded by a real-time limit.  A workgroup that runs out of
-// time (only possible if the grid is not all resident) raises an error word,
-// fills x with NaN and leaves; the others then see the error word and leave.
+// Every wait is bounded by a real-time limit (the caller's, 1 s by default).
+// A workgroup that runs out of time (only possible if the grid is not all
+// resident, or if the caller set a limit shorter than a phase) raises an
+// error word, fills x with NaN and leaves; the others then see the error word
+// and leave.  The host reads the word back through the status call.
 // The host launches at most one workgroup per compute unit.
 #include <type_traits>
 
@@ -60,7 +62,8 @@ constexpr int kNH = kMaxH / 2 / kR;           // 2-element chunks per receiver, 
 constexpr int kNF = kMaxF / 2 / kR;           // 2-element chunks per receiver, length F
 constexpr int kMaxLayers = 16;                // layers per launch (kernel-argument table)
 constexpr int kMaxGrid = 512;
-constexpr uint64_t kTimeoutTicks = 100000000ull;   // 1 s of the 100 MHz real-time counter
+constexpr uint64_t kTicksPerUs = 100;        // the real-time counter runs at 100 MHz
+constexpr uint64_t kDefaultWaitUs = 1000000;  // 1 s
 constexpr int kSC1 = 16;                      // buffer cache policy: coherent at device scope
 
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -87,6 +90,7 @@ struct PArgs {
     uint2 *xa, *xm, *v, *o, *h, *y;           // tagged (value bits, tag), slot 0
     int slot_stride;                          // tagged values per layer slot
     unsigned *err;
+    uint64_t wait_ticks;                      // limit of every wait
 };
 
 // tag of the values produced in phase p of global layer lg (0 = cleared)
@@ -239,7 +243,7 @@ __device__ __forceinline__ bool receive(const PArgs &a, const uint2 *p0, unsigne
                 rdy = w0.y == t0 && w0.w == t0 && (!TWO || (w1.y == t1 && w1.w == t1));
             }
             if (__shfl(rdy, 0)) break;
-            if (ld_u(a.err) != 0u || __builtin_amdgcn_s_memrealtime() - start > kTimeoutTicks)
+            if (ld_u(a.err) != 0u || __builtin_amdgcn_s_memrealtime() - start > a.wait_ticks)
                 return false;
         }
     }
@@ -271,7 +275,7 @@ __device__ __forceinline__ bool receive(const PArgs &a, const uint2 *p0, unsigne
     while (pending) {
         sweep(std::integral_constant<int, kSC1>{});
         if (pending && (ld_u(a.err) != 0u ||
-                        __builtin_amdgcn_s_memrealtime() - start > kTimeoutTicks))
+                        __builtin_amdgcn_s_memrealtime() - start > a.wait_ticks))
             return false;
     }
     return true;
@@ -700,14 +704,24 @@ size_t stack_persistent_ws_floats(int H, int KV, int F) {
     return 2 * (size_t)kMaxLayers * (4 * (size_t)H + KV + F) + 64;
 }
 
+unsigned *stack_status_word(const StackWs &ws, int H, int KV, int F) {
+    uint2 *t = reinterpret_cast<uint2 *>(ws.tagged);
+    return reinterpret_cast<unsigned *>(t + (size_t)kMaxLayers * (4 * (size_t)H + KV + F));
+}
+
+hipError_t launch_stack_clear_status(unsigned *err, hipStream_t s) {
+    hipLaunchKernelGGL(stack_reset_kernel, dim3(1), dim3(256), 0, s, (uint2 *)nullptr, 0, err);
+    return hipGetLastError();
+}
+
 bool stack_persistent_fits(int H, int KV, int F, int D) {
     int ls[4], ns[4];
     return plan(grid_for_device(), H, KV, F, D, ls, ns);
 }
 
 hipError_t launch_decode_stack_persistent(const StackLayer *layers, int n_layers, int H, int KV,
-                                          int F, int D, float eps, float *x, float *trace,
-                                          const StackWs &ws, hipStream_t s) {
+                                          int F, int D, float eps, int wait_us, float *x,
+                                          float *trace, const StackWs &ws, hipStream_t s) {
     const int G = grid_for_device();
     PArgs a = {};
     if (!plan(G, H, KV, F, D, a.lshift, a.nslot))
@@ -720,7 +734,8 @@ hipError_t launch_decode_stack_persistent(const StackLayer *layers, int n_layers
     a.xa = t; a.xm = t + H; a.o = t + 2 * H; a.y = t + 3 * H; a.v = t + 4 * H; a.h = t + 4 * H + KV;
     a.slot_stride = 4 * H + KV + F;
     const int n_tagged = kMaxLayers * a.slot_stride;
-    a.err = reinterpret_cast<unsigned *>(t + n_tagged);
+    a.err = stack_status_word(ws, H, KV, F);
+    a.wait_ticks = (wait_us > 0 ? (uint64_t)wait_us : kDefaultWaitUs) * kTicksPerUs;
     hipLaunchKernelGGL(stack_reset_kernel, dim3(256), dim3(256), 0, s, t, n_tagged, a.err);
     for (int l0 = 0; l0 < n_layers; l0 += kMaxLayers) {
         const int n = n_layers - l0 < kMaxLayers ? n_layers - l0 : kMaxLayers;

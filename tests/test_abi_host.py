@@ -51,15 +51,17 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.bl_abi_version() == 1
+    assert lib.bl_abi_version() == 2
     for code, name in _native.STATUS.items():
         assert lib.bl_status_string(code).decode() == name
     assert lib.bl_status_string(99).decode() == "BL_ERR_UNKNOWN"
 
 
 def test_workspace_sizes(lib):
-    assert lib.bl_workspace_bytes(bl.BL_OP_QUANT_WEIGHT, 0, 6912, 2560, 0) == 6912 * 8
+    # one fp64 sum per block of 2048 row-major weights, rounded up to 256 bytes
+    assert lib.bl_workspace_bytes(bl.BL_OP_QUANT_WEIGHT, 0, 6912, 2560, 0) == 6912 * 2560 // 2048 * 8
     assert lib.bl_workspace_bytes(bl.BL_OP_QUANT_WEIGHT, 0, 7, 2560, 0) == 256
+    assert lib.bl_workspace_bytes(bl.BL_OP_QUANT_WEIGHT, 0, 40, 4096, 0) == 768
     M, F = 2048, 6912
     ws = lib.bl_workspace_bytes(bl.BL_OP_FFN_RELU2, M, 2560, 2560, F)
     assert ws >= M * F * (4 + 4 + 1) + 2 * M * 4
@@ -234,10 +236,10 @@ def test_stack_validation(lib):
     assert need >= 4 * (2 * 256 + 2 * 128 + 2 * 512) + 512
 
     def call(layers=None, n=None, H=256, KV=128, F=512, Dh=64, eps=1e-5, path=0,
-             x=A16, trace=None, ws=A16, wsb=1 << 20):
+             x=A16, trace=None, ws=A16, wsb=1 << 20, wait_us=0, reserved=0):
         layers = [layer()] if layers is None else layers
         arr = (Lr * max(1, len(layers)))(*layers)
-        dims = D(H, KV, F, Dh, eps, path)
+        dims = D(H, KV, F, Dh, eps, path, wait_us, reserved)
         return lib.bitlinear_decode_stack(arr, len(layers) if n is None else n,
                                           ctypes.byref(dims), x, trace, ws, wsb, None)
 
@@ -253,6 +255,8 @@ def test_stack_validation(lib):
     assert call(eps=float("nan")) == SHAPE
     assert call(path=3) == SHAPE
     assert call(path=-1) == SHAPE
+    assert call(wait_us=-1) == SHAPE
+    assert call(reserved=1) == SHAPE
     assert call(n=0, x=None) == OK                    # no layers: nothing to do
     assert call(x=None) == NULL
     assert call(layers=[layer(), layer(Wd=None)]) == NULL
@@ -265,6 +269,28 @@ def test_stack_validation(lib):
     assert call(wsb=need - 1) == WS
     assert call(ws=None) == WS
     assert call(ws=A4) == ALIGN
+
+
+def test_stack_status_validation(lib):
+    """The status call checks everything on the host before it reads a byte."""
+    D = _native.StackDims
+    need = bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, 256, 128, 512)
+    out = ctypes.c_int32(-5)
+
+    def call(H=256, ws=A16, wsb=1 << 20, status=True, wait_us=0, reserved=0, dims=True):
+        d = D(H, 128, 512, 64, 1e-5, 0, wait_us, reserved)
+        return lib.bitlinear_decode_stack_status(ws, wsb, ctypes.byref(d) if dims else None,
+                                                 ctypes.byref(out) if status else None)
+
+    assert call(dims=False) == NULL
+    assert call(H=200) == SHAPE
+    assert call(wait_us=-2) == SHAPE
+    assert call(reserved=3) == SHAPE
+    assert call(status=False) == NULL
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ws=A4) == ALIGN
+    assert out.value == -5                            # nothing written on an error
 
 
 def test_backward_validation(lib):

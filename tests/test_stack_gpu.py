@@ -1,12 +1,18 @@
 """GPU parity of bitlinear_decode_stack against the oracle's decode stack.
 
-The oracle runs the whole stack on its own weights and its own activations
-(oracle.decode_stack).  Each value that feeds a later per-token quantisation
-is carried in fp32 on both sides, so the first layer, which depends on x only
-through the same fp32 operations, must be bit-identical.  Later layers pass
-through the subln RMS (an fp64 sum whose order differs between the two
-sides); there the bar is 1e-3 relative to each trace segment's largest
-magnitude, and nearly every element is still expected to be bit-identical.
+Teacher-forced (the primary check): the GPU runs the whole stack with its
+per-layer trace; the oracle then runs each layer alone from the GPU's input
+to that layer (oracle.decode_stack on one layer).  Every value that feeds a
+later per-token quantisation is carried in fp32 on both sides, so q, k, v, o
+and x_mid must be bit-identical in every layer; the FFN output y carries the
+subln RMS, an fp64 sum whose order is each side's own, and must be within
+1e-3 relative of the oracle's, element by element; the next layer's input
+and the final x must be the fp32 sums x_mid + y of the GPU's own values.
+
+Free-running (secondary): the oracle runs the whole stack on its own
+activations; the first layer must be bit-identical, later layers within 1e-3
+of each trace segment's largest magnitude (a y that differs in its last bit
+can move a later int8 decision by one step).
 """
 import numpy as np
 import pytest
@@ -43,6 +49,34 @@ def _build(bl, seed, n_layers, H, KV, F, gain=True):
         gpu_layers.append(G)
         ref_layers.append(R)
     return gpu_layers, ref_layers
+
+
+SEGMENTS = ("x_in", "q", "k", "v", "o", "x_mid", "y")
+
+
+def _segments(row, H, KV):
+    cuts = np.cumsum([0, H, H, KV, KV, H, H, H])
+    return {n: row[cuts[i]:cuts[i + 1]] for i, n in enumerate(SEGMENTS)}
+
+
+def _teacher_forced(trace, x_final, layers, H, KV, F, D, eps=1e-5):
+    """Each layer of the GPU trace against the oracle run on that layer alone,
+    from the GPU's input to it."""
+    n = trace.shape[0]
+    u = lambda a: np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    for l in range(n):
+        got = _segments(trace[l], H, KV)
+        _, ref_row = oracle.decode_stack(got["x_in"].copy(), [layers[l]], H, KV, F, D, eps)
+        ref = _segments(ref_row[0], H, KV)
+        for name in ("q", "k", "v", "o", "x_mid"):
+            diff = u(got[name]) != u(ref[name])
+            assert not diff.any(), (l, name, int(diff.sum()))
+        err = np.abs(got["y"].astype(np.float64) - ref["y"].astype(np.float64))
+        bad = err > RTOL * np.abs(ref["y"].astype(np.float64))
+        assert not bad.any(), (l, "y", int(bad.sum()), float(err.max()))
+        x_next = np.add(got["x_mid"], got["y"], dtype=np.float32)
+        following = trace[l + 1, :H] if l + 1 < n else x_final
+        assert np.array_equal(u(following), u(x_next)), (l, "x_next")
 
 
 def _compare(trace, ref_trace, H, KV):
@@ -153,6 +187,70 @@ def test_decode_stack_chunked_layers(gpu):
     _compare(trace.cpu().numpy(), ref_trace, H, KV)
     err = np.abs(x.cpu().numpy().astype(np.float64) - ref_x).max()
     assert err <= RTOL * np.abs(ref_x).max()
+
+
+@PATHS
+def test_decode_stack_teacher_forced_30_layers(gpu, path):
+    """The 2B-class stack as timed (30 layers at 2560 / 640 / 6912, head size
+    128; the persistent path runs it as 16 + 14 layers in two launches, and
+    reuses its 16 layer slots), every layer checked teacher-forced.  Three
+    quantised layers are cycled over the 30 to keep the setup short."""
+    bl = gpu
+    H, KV, F, D = workloads.HIDDEN, workloads.KV, workloads.FFN, workloads.HEAD_DIM
+    n = workloads.LAYERS
+    gl, rl = _build(bl, 41, 3, H, KV, F)
+    gl = [gl[l % 3] for l in range(n)]
+    rl = [rl[l % 3] for l in range(n)]
+    x0 = workloads.stack_token(41, H)
+    x = x0.cuda()
+    ws = torch.empty(bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, H, KV, F), dtype=torch.uint8,
+                     device="cuda")
+    trace = bl.bitlinear_decode_stack(gl, x, H, KV, F, D, eps=1e-5, trace=True, ws=ws, path=path)
+    torch.cuda.synchronize()
+    assert bl.bitlinear_decode_stack_status(ws, H, KV, F, D, path=path) == 0
+    trace = trace.cpu().numpy()
+    assert np.array_equal(trace[0, :H].view(np.uint32), x0.numpy().view(np.uint32))
+    _teacher_forced(trace, x.cpu().numpy(), rl, H, KV, F, D)
+
+
+@PATHS
+def test_decode_stack_teacher_forced_small(gpu, path):
+    """Teacher-forced on the small dimension sets, 18 layers (two persistent
+    launches), subln gain on."""
+    bl = gpu
+    H, KV, F, D, n = 256, 64, 448, 32, 18
+    gl, rl = _build(bl, 45, n, H, KV, F)
+    x0 = workloads.stack_token(45, H)
+    x = x0.cuda()
+    trace = bl.bitlinear_decode_stack(gl, x, H, KV, F, D, trace=True, path=path)
+    torch.cuda.synchronize()
+    _teacher_forced(trace.cpu().numpy(), x.cpu().numpy(), rl, H, KV, F, D)
+
+
+def test_decode_stack_status_after_time_out(gpu):
+    """A wait limit of 1 us, far shorter than one exchange of the persistent
+    path, makes waits give up: the kernel still exits, x is NaN and the status
+    call reports it; the next call with the default limit clears the status."""
+    bl = gpu
+    H, KV, F, D = 512, 128, 1024, 64
+    gl, _ = _build(bl, 47, 2, H, KV, F)
+    x0 = workloads.stack_token(47, H).cuda()
+    ws = torch.empty(bl.workspace_bytes(bl.BL_OP_DECODE_STACK, 1, H, KV, F), dtype=torch.uint8,
+                     device="cuda")
+    x = x0.clone()
+    bl.bitlinear_decode_stack(gl, x, H, KV, F, D, ws=ws, path=bl.BL_STACK_PERSISTENT, wait_us=1)
+    torch.cuda.synchronize()
+    assert bl.bitlinear_decode_stack_status(ws, H, KV, F, D) == 1
+    assert torch.isnan(x).all()
+    x = x0.clone()
+    bl.bitlinear_decode_stack(gl, x, H, KV, F, D, ws=ws, path=bl.BL_STACK_PERSISTENT)
+    torch.cuda.synchronize()
+    assert bl.bitlinear_decode_stack_status(ws, H, KV, F, D) == 0
+    assert torch.isfinite(x).all()
+    x = x0.clone()
+    bl.bitlinear_decode_stack(gl, x, H, KV, F, D, ws=ws, path=bl.BL_STACK_LAUNCHES)
+    torch.cuda.synchronize()
+    assert bl.bitlinear_decode_stack_status(ws, H, KV, F, D) == 0
 
 
 def test_decode_stack_paths_agree_full_dims(gpu):
