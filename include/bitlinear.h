@@ -119,6 +119,24 @@ bl_status quant_weight_absmean_pack(const float *W, int64_t N, int64_t K,
                                     void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * quant_weight_absmean_pack_noalloc -- for callers that cannot allocate:
+ * code under HIP graph capture, and serving or training loops (which
+ * re-quantise the latent weights every step) that forbid allocation.
+ * Same arguments (without ws), formats, bits and errors as
+ * quant_weight_absmean_pack, whose kernels it runs; its fp64 block sums go to
+ * a device array the library owns (512 KiB on each GPU it runs on, held until
+ * the process ends) instead of a caller workspace.  Allocates nothing.
+ *   N*K <= BL_NOALLOC_MAX_WEIGHTS (2^27), else BL_ERR_SHAPE.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (e.g. on two streams) race and must be serialised by the caller.  Each
+ * call writes every block sum it reads before reading it.
+ */
+#define BL_NOALLOC_MAX_WEIGHTS (1LL << 27)
+
+bl_status quant_weight_absmean_pack_noalloc(const float *W, int64_t N, int64_t K,
+                                            uint8_t *Wp, float *gamma, void *stream);
+
+/* ------------------------------------------------------------------------
  * quant_act_absmax_i8 -- per-token absmax int8 activation quantisation.
  * [NEWS] 权重映射为三元值; [CARD] 模型详情 (per-token absmax, 8-bit).
  *

@@ -11,5 +11,5 @@ from ._native import (  # noqa: F401
     GemvJob, Layer, StackDims, bitlinear_backward_input, bitlinear_backward_weight,
     bitlinear_decode_stack, bitlinear_decode_stack_status, bitlinear_ffn_relu2, bitlinear_gemm, bitlinear_gemv,
     bitlinear_gemv_fused, bitlinear_gemv_t5, bitlinear_repack_t5, load, quant_act_absmax_i8,
-    quant_weight_absmean_pack, t5_row_bytes, workspace_bytes,
+    quant_weight_absmean_pack, quant_weight_absmean_pack_noalloc, t5_row_bytes, workspace_bytes,
 )

@@ -24,7 +24,7 @@ BL_MAX_K = 131072
 STATUS = {0: "BL_OK", 1: "BL_ERR_NULL", 2: "BL_ERR_SHAPE", 3: "BL_ERR_DTYPE",
           4: "BL_ERR_ALIGN", 5: "BL_ERR_WORKSPACE", 6: "BL_ERR_ARCH", 7: "BL_ERR_HIP"}
 
-EXPORTS = ["quant_weight_absmean_pack", "quant_act_absmax_i8", "bitlinear_gemv",
+EXPORTS = ["quant_weight_absmean_pack", "quant_weight_absmean_pack_noalloc", "quant_act_absmax_i8", "bitlinear_gemv",
            "bitlinear_gemm", "bitlinear_gemv_fused", "bitlinear_ffn_relu2",
            "bitlinear_decode_stack", "bitlinear_decode_stack_status",
            "bitlinear_backward_input", "bitlinear_backward_weight",
@@ -86,6 +86,8 @@ def load():
     st = ctypes.c_int
     lib.quant_weight_absmean_pack.restype = st
     lib.quant_weight_absmean_pack.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
+    lib.quant_weight_absmean_pack_noalloc.restype = st
+    lib.quant_weight_absmean_pack_noalloc.argtypes = [_p, _i64, _i64, _p, _p, _p]
     lib.quant_act_absmax_i8.restype = st
     lib.quant_act_absmax_i8.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p]
     for name in ("bitlinear_gemv", "bitlinear_gemm"):
@@ -170,6 +172,22 @@ def quant_weight_absmean_pack(W, Wp=None, gamma=None, ws=None, stream=None):
         ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
     _check("quant_weight_absmean_pack", load().quant_weight_absmean_pack(
         _ptr(W), N, K, _ptr(Wp), _ptr(gamma), _ptr(ws), ws.numel(), _stream(stream)))
+    return Wp, gamma
+
+
+def quant_weight_absmean_pack_noalloc(W, Wp=None, gamma=None, stream=None):
+    """quant_weight_absmean_pack with the library's own scratch (no workspace);
+    N * K <= 2^27.  Pass Wp and gamma to keep the call itself free of
+    allocation (torch allocates them here when they are absent)."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    dev = W.device
+    Wp = _dev(Wp, torch.uint8, "Wp") if Wp is not None else torch.empty(
+        (N, K // 4), dtype=torch.uint8, device=dev)
+    gamma = _dev(gamma, torch.float32, "gamma") if gamma is not None else torch.empty(
+        (1,), dtype=torch.float32, device=dev)
+    _check("quant_weight_absmean_pack_noalloc", load().quant_weight_absmean_pack_noalloc(
+        _ptr(W), N, K, _ptr(Wp), _ptr(gamma), _stream(stream)))
     return Wp, gamma
 
 

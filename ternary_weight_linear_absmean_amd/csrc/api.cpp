@@ -203,6 +203,41 @@ BL_EXPORT bl_status quant_weight_absmean_pack(const float *W, int64_t N, int64_t
                     name);
 }
 
+BL_EXPORT bl_status quant_weight_absmean_pack_noalloc(const float *W, int64_t N, int64_t K,
+                                                      uint8_t *Wp, float *gamma, void *stream) {
+    const char *name = "quant_weight_absmean_pack_noalloc";
+    if (N < 0 || K < 0 || K % 4 != 0 || K > BL_MAX_K || N > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: need N in [0, 2^31), K in [0, %d] with K %% 4 == 0 "
+                    "(N=%lld K=%lld)", name, BL_MAX_K, (long long)N, (long long)K);
+    if (N * K > BL_NOALLOC_MAX_WEIGHTS)
+        return fail(BL_ERR_SHAPE, "%s: N*K=%lld exceeds the %lld weights its scratch holds",
+                    name, (long long)(N * K), (long long)BL_NOALLOC_MAX_WEIGHTS);
+    if (!gamma)
+        return fail(BL_ERR_NULL, "%s: gamma is NULL", name);
+    if (!aligned(gamma, 4))
+        return fail(BL_ERR_ALIGN, "%s: gamma must be 4-byte aligned", name);
+    if (N > 0 && K > 0) {
+        if (!W || !Wp)
+            return fail(BL_ERR_NULL, "%s: NULL pointer (W=%p Wp=%p)", name, (const void *)W,
+                        (const void *)Wp);
+        if (!aligned(W, 16) || !aligned(Wp, 16))
+            return fail(BL_ERR_ALIGN, "%s: W and Wp must be 16-byte aligned", name);
+    }
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+    static_assert(BL_NOALLOC_MAX_WEIGHTS / 2048 <= bl::kNoAllocQuantMaxBlocks,
+                  "the scratch array holds every block sum");
+    double *bsum = nullptr;
+    const hipError_t e = bl::noalloc_quant_scratch(&bsum);
+    if (e != hipSuccess)
+        return fail(BL_ERR_HIP, "%s: scratch address lookup failed: %s", name,
+                    hipGetErrorString(e));
+    return launched(bl::launch_quant_weight(W, N, K, Wp, gamma, bsum,
+                                            static_cast<hipStream_t>(stream)),
+                    name);
+}
+
 BL_EXPORT bl_status quant_act_absmax_i8(const void *X, bl_dtype dtype, int64_t M, int64_t K,
                                         int8_t *Xq, float *d, void *stream) {
     const char *name = "quant_act_absmax_i8";

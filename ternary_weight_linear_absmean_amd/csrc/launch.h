@@ -16,6 +16,11 @@ namespace bl {
 int64_t quant_weight_blocks(int64_t N, int64_t K);
 hipError_t launch_quant_weight(const float *W, int64_t N, int64_t K, uint8_t *Wp,
                                float *gamma, double *bsum, hipStream_t s);
+// The allocation-free variant's block sums live in a library-owned device
+// array of kNoAllocQuantMaxBlocks doubles (512 KiB: N*K <= 2^27 weights);
+// noalloc_quant_scratch gives the current device's address of it.
+constexpr int64_t kNoAllocQuantMaxBlocks = 65536;
+hipError_t noalloc_quant_scratch(double **out);
 
 // Per-token absmax int8 quantisation; dtype 0 = fp32, 1 = bf16.
 hipError_t launch_quant_act(const void *X, int dtype, int64_t M, int64_t K,

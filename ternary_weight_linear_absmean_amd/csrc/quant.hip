@@ -6,6 +6,8 @@
 //   (technical-report copy, 推理完满 / GPU端).
 // Activations (iaiol.com article, 权重映射为三元值; model card, 模型详情):
 //   per-token absmax int8.
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -300,6 +302,39 @@ hipError_t launch_quant_weight(const float *W, int64_t N, int64_t K, uint8_t *Wp
     const unsigned nb_pack = (unsigned)((bytes + 255) / 256);
     hipLaunchKernelGGL(ternarize_pack_kernel, dim3(nb_pack), dim3(256), 0, s, W, N, K, gamma, Wp);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch for the allocation-free weight quantiser: the fp64
+// block sums, one per 2048 weights.  Every GPU the library runs on holds its
+// own copy until the process ends.  Host code never passes the array's name to
+// a kernel (in host code it is a stand-in, not a device address): the device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) double scratch[kNoAllocQuantMaxBlocks];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+double *g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t noalloc_quant_scratch(double **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = static_cast<double *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_quant_act(const void *X, int dtype, int64_t M, int64_t K, int8_t *Xq, float *d,

@@ -94,6 +94,23 @@ def test_product_validation(lib):
     assert lib.bitlinear_gemv(A16, A4, 65, A16, A4, 8, 64, A4, None, None) == SHAPE
 
 
+def test_noalloc_quant_validation(lib):
+    """The allocation-free quantiser's host checks: its scratch holds the
+    block sums of at most 2^27 weights."""
+    f = lib.quant_weight_absmean_pack_noalloc
+    assert f(A16, -1, 64, A16, A4, None) == SHAPE
+    assert f(A16, 2, 66, A16, A4, None) == SHAPE                          # K % 4
+    assert f(A16, 2, 2 * bl.BL_MAX_K, A16, A4, None) == SHAPE
+    assert f(A16, 32769, 4096, A16, A4, None) == SHAPE                    # N K > 2^27
+    assert "2^27" in _err(lib) or "134217728" in _err(lib)
+    assert f(A16, 2, 64, A16, None, None) == NULL
+    assert f(None, 2, 64, A16, A4, None) == NULL
+    assert f(A16, 2, 64, None, A4, None) == NULL
+    assert f(A4, 2, 64, A16, A4, None) == ALIGN
+    assert f(A16, 2, 64, A4, A4, None) == ALIGN
+    assert f(A16, 2, 64, A16, A1, None) == ALIGN
+
+
 def test_t5_validation(lib):
     rb, rp, gv = lib.bitlinear_t5_row_bytes, lib.bitlinear_repack_t5, lib.bitlinear_gemv_t5
     # rows: ceil(K / 5) bytes rounded up to 16
