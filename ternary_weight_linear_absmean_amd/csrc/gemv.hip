@@ -179,14 +179,24 @@ hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
 // Fused decode kernel: per-token absmax int8 quantisation folded into the
 // GEMV, for several independent BitLinears in one launch.  Workgroups are
 // dealt to jobs in order (job j owns workgroups [wg_begin_j, wg_begin_j+1)).
-// Each workgroup
-//   1. issues its first packed-weight loads (they need no activations),
-//   2. reads the job's activation rows (L2-resident after the first
-//      workgroup), forms max |x| per token with a block reduction, and
-//      writes the int8 codes straight into LDS in transposed 16-byte groups
-//      (the first workgroup of the job also stores Xq and d to memory),
-//   3. runs the same unit loop and lane reduction as gemv_kernel, with the
-//      lane split L chosen per job.
+// A workgroup's waves have two roles:
+//   quantising waves (4) read the job's activation rows (L2-resident after
+//     the first workgroup), form max |x| per token and write the int8 codes
+//     into LDS in transposed 16-byte groups (the job's first workgroup also
+//     stores Xq and d to memory); they publish each step by counting up an
+//     LDS word;
+//   compute waves (8) issue all their packed-weight loads at once, wait for
+//     the codes count, then run the unit loop and lane reduction of
+//     gemv_kernel, with the lane split L chosen per job.
+// The roles are split because a wave cannot issue past a load instruction
+// the memory pipeline has not accepted: with the weight requests of the whole
+// launch in flight, a wave that issued weight loads reaches the next
+// instruction only as the earliest of them return.  A workgroup barrier
+// between the activation and the weight phases therefore delayed the codes
+// to about when the weights had landed (codes 3.1 us after the workgroup
+// start, 2.9 us of which waiting); with the quantising waves issuing no
+// weight loads and no barrier, the four decode shapes' step went from 7.2 to
+// 6.35 us.
 struct FusedJob {
     const void *X;
     const uint8_t *Wp;
@@ -203,14 +213,14 @@ struct FusedArgs {
     int count, M;
 };
 
-// 512 threads: every workgroup quantises its job's whole activation row, so
-// fewer, larger workgroups repeat that less; on the four 2B-class decode
-// shapes (M = 1) 512 measured 9.3 us per step against 9.7 us for 256 and
-// 11.4 us for 1024 (fewer workgroups than compute units can take evenly).
-#ifndef BL_FUSED_THREADS
-#define BL_FUSED_THREADS 512
-#endif
-constexpr int kFThreads = BL_FUSED_THREADS;
+// 512 compute threads: every workgroup quantises its job's whole activation
+// row, so fewer, larger workgroups repeat that less; on the four 2B-class
+// decode shapes (M = 1) 512 measured 9.3 us per step against 9.7 us for 256
+// and 11.4 us for 1024 (before the role split).
+constexpr int kQWaves = 4;                     // waves that quantise the activations
+constexpr int kQThreads = 64 * kQWaves;
+constexpr int kCThreads = 512;                 // waves that load weights and form the products
+constexpr int kFThreads = kQThreads + kCThreads;
 // Every 16-byte weight unit of a lane is requested at once: with the lane
 // splits below a lane owns at most 108 / 16 < 8 units of a row.
 constexpr int kFUnits = 8;
@@ -262,8 +272,9 @@ __device__ __forceinline__ void unpack_x16(const uint4 (&raw)[4], int dtype, flo
 // are added with shuffles.
 template <int MT, bool kMfma>
 __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs args) {
-    extern __shared__ uint4 xs[];   // [MT][K / 16] transposed code groups, then [MT][K] fp32
-    __shared__ float red[kFThreads / 64][MT];
+    extern __shared__ uint4 xs[];   // [MT][K / 16] transposed code groups, then the raw activations
+    __shared__ float red[kQWaves][MT];
+    __shared__ unsigned n_amax, n_codes;        // quantising waves past each step
     int j = 0;
     for (int t = 1; t < args.count; ++t)
         if ((int)blockIdx.x >= args.job[t].wg_begin) j = t;
@@ -271,145 +282,153 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     const int K = jb.K, N = jb.N, dtype = jb.dtype, lshift = jb.lshift;
     // gamma now, not after the dot products (a job with no rows has none)
     const float gam = N > 0 ? scalar_load(jb.gamma) : 0.0f;
-    const int L = 1 << lshift;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int r = lane >> lshift;
-    const int s = lane & (L - 1);
     const int wg = (int)blockIdx.x - jb.wg_begin;
-    const int rows_wg = (kFThreads / 64) * (64 >> lshift);
-    // the lane's row, first unit and unit stride
-    int row, sig, stride;
-    if constexpr (kMfma) {
-        const int c = L >> 2, i = lane & 15;                 // columns per row, column
-        row = wg * rows_wg + (tid >> 6) * (64 >> lshift) + i / c;
-        sig = i % c + c * (lane >> 4);
-        stride = L;
-    } else {
-        row = wg * rows_wg + (tid >> 6) * (64 >> lshift) + r;
-        sig = s;
-        stride = L;
-    }
     const int m0 = blockIdx.y * MT;
     const int mt = min(MT, args.M - m0);
     const int U = K / 64;
     const int gpc = K / 16;
-    const uint4 *wrow = reinterpret_cast<const uint4 *>(jb.Wp + (size_t)max(min(row, N - 1), 0) * (K / 4));
-
-    // 1. Issue order matters: vector-memory loads retire in order, so the
-    //    first activation groups of this thread are requested before the
-    //    packed-weight loads; waiting for the activations then leaves the
-    //    weights in flight while the quantisation runs.
-    const int gsz = dtype == 0 ? 4 : 2;                       // uint4 per 16 elements
-    uint4 *xraw = xs + MT * gpc;                               // [MT][K / 16][gsz]
-    const char *xbase = reinterpret_cast<const char *>(jb.X);
-    const int ng = mt * gpc;                                   // (token, group) pairs
-    uint4 xr[kXPre][4];
-    // Both load sets are unconditional (clamped to valid addresses) so the
-    // wait for the activations can leave exactly the weight loads pending.
-#pragma unroll
-    for (int p = 0; p < kXPre; ++p) {
-        const int e = min(tid + p * kFThreads, ng - 1);
-        const int m = e / gpc, g = e - m * gpc;
-        // token row m0 + m starts K * (element size) = K * gsz bytes apart
-        const uint4 *src = reinterpret_cast<const uint4 *>(xbase + (size_t)(m0 + m) * K * gsz) +
-                           (size_t)g * gsz;
-        if (dtype == 0) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xr[p][t] = src[t];
-        } else {
-            xr[p][0] = src[0];
-            xr[p][1] = src[1];
-        }
+    if (tid == 0) {
+        n_amax = 0u;
+        n_codes = 0u;
     }
+    __syncthreads();                            // nothing is in flight yet
+
+    if (tid < kQThreads) {
+        // ---- quantising waves: the job's activation rows -> int8 codes in LDS
+        const int gsz = dtype == 0 ? 4 : 2;                       // uint4 per 16 elements
+        uint4 *xraw = xs + MT * gpc;                               // [MT][K / 16][gsz]
+        const char *xbase = reinterpret_cast<const char *>(jb.X);
+        const int ng = mt * gpc;                                   // (token, group) pairs
+        uint4 xr[kXPre][4];
+#pragma unroll
+        for (int p = 0; p < kXPre; ++p) {
+            const int e = min(tid + p * kQThreads, ng - 1);
+            const int m = e / gpc, g = e - m * gpc;
+            const uint4 *src = reinterpret_cast<const uint4 *>(xbase + (size_t)(m0 + m) * K * gsz) +
+                               (size_t)g * gsz;
+            if (dtype == 0) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) xr[p][t] = src[t];
+            } else {
+                xr[p][0] = src[0];
+                xr[p][1] = src[1];
+            }
+        }
+        float amax[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) amax[m] = 0.0f;
+        auto stage = [&](const uint4 (&raw)[4], int e) {
+            const int m = e / gpc, g = e - m * gpc;
+            float x[16];
+            unpack_x16(raw, dtype, x);
+            uint4 *dst = xraw + ((size_t)m * gpc + g) * gsz;
+            dst[0] = raw[0];
+            dst[1] = raw[1];
+            if (dtype == 0) { dst[2] = raw[2]; dst[3] = raw[3]; }
+            float a = 0.0f;
+#pragma unroll
+            for (int i2 = 0; i2 < 16; ++i2) a = fmaxf(a, fabsf(x[i2]));
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+                if (mm == m) amax[mm] = fmaxf(amax[mm], a);
+        };
+#pragma unroll
+        for (int p = 0; p < kXPre; ++p) {
+            const int e = tid + p * kQThreads;
+            if (e < ng) stage(xr[p], e);
+        }
+        for (int e = tid + kXPre * kQThreads; e < ng; e += kQThreads) {
+            const int m = e / gpc, g = e - m * gpc;
+            const uint4 *src = reinterpret_cast<const uint4 *>(xbase + (size_t)(m0 + m) * K * gsz) +
+                               (size_t)g * gsz;
+            uint4 raw[4];
+            raw[0] = src[0];
+            raw[1] = src[1];
+            if (dtype == 0) { raw[2] = src[2]; raw[3] = src[3]; }
+            stage(raw, e);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                amax[m] = fmaxf(amax[m], __shfl_xor(amax[m], off));
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) red[tid >> 6][m] = amax[m];
+        }
+        // every quantising wave's maximum (and raw words) in LDS before the count
+        if (lane == 0)
+            __hip_atomic_fetch_add(&n_amax, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        while (__hip_atomic_load(&n_amax, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kQWaves)
+            __builtin_amdgcn_s_sleep(1);
+        const bool writer = (wg == 0);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float a = red[0][m];
+#pragma unroll
+            for (int v = 1; v < kQWaves; ++v) a = fmaxf(a, red[v][m]);
+            if (m < mt) {
+                const float sc = act_inv_scale(a);
+                for (int g = tid; g < gpc; g += kQThreads) {
+                    uint4 raw[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (t < gsz) raw[t] = xraw[((size_t)m * gpc + g) * gsz + t];
+                    float x[16];
+                    unpack_x16(raw, dtype, x);
+                    uint32_t q4[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        q4[t] = (uint32_t)(act_code(x[4 * t], sc) & 0xFF) |
+                                ((uint32_t)(act_code(x[4 * t + 1], sc) & 0xFF) << 8) |
+                                ((uint32_t)(act_code(x[4 * t + 2], sc) & 0xFF) << 16) |
+                                ((uint32_t)(act_code(x[4 * t + 3], sc) & 0xFF) << 24);
+                    const uint4 qv = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+                    if (writer && jb.Xq)
+                        *reinterpret_cast<uint4 *>(jb.Xq + (size_t)(m0 + m) * K + 16 * g) = qv;
+                    xs[m * gpc + g] = transpose16(qv);
+                }
+                if (writer && jb.d && tid == 0)
+                    jb.d[m0 + m] = act_scale(a);
+            }
+        }
+        // the codes in LDS before the count the compute waves wait for
+        if (lane == 0)
+            __hip_atomic_fetch_add(&n_codes, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return;
+    }
+
+    // ---- compute waves: issue the packed-weight loads, then wait for the codes
+    const int ct = tid - kQThreads;
+    const int L = 1 << lshift;
+    const int r = lane >> lshift;
+    const int s = lane & (L - 1);
+    const int rows_wg = (kCThreads / 64) * (64 >> lshift);
+    int row, sig;
+    if constexpr (kMfma) {
+        const int c = L >> 2, i = lane & 15;                 // columns per row, column
+        row = wg * rows_wg + (ct >> 6) * (64 >> lshift) + i / c;
+        sig = i % c + c * (lane >> 4);
+    } else {
+        row = wg * rows_wg + (ct >> 6) * (64 >> lshift) + r;
+        sig = s;
+    }
+    const uint4 *wrow = reinterpret_cast<const uint4 *>(jb.Wp + (size_t)max(min(row, N - 1), 0) * (K / 4));
     uint4 w[kFUnits];
 #pragma unroll
     for (int q = 0; q < kFUnits; ++q)
-        w[q] = ld_stream(wrow + min(sig + q * stride, U - 1));  // a job with N == 0 reads its own X here
-
-    // 2. activation quantisation into LDS: keep each group's raw words in LDS
-    //    and form max |x| per token; then quantise from LDS.
-    float amax[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) amax[m] = 0.0f;
-    // stage one group: raw words to LDS, fold max |x| into its token's amax
-    auto stage = [&](const uint4 (&raw)[4], int e) {
-        const int m = e / gpc, g = e - m * gpc;
-        float x[16];
-        unpack_x16(raw, dtype, x);
-        uint4 *dst = xraw + ((size_t)m * gpc + g) * gsz;
-        dst[0] = raw[0];
-        dst[1] = raw[1];
-        if (dtype == 0) { dst[2] = raw[2]; dst[3] = raw[3]; }
-        float a = 0.0f;
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) a = fmaxf(a, fabsf(x[i2]));
-#pragma unroll
-        for (int mm = 0; mm < MT; ++mm)
-            if (mm == m) amax[mm] = fmaxf(amax[mm], a);
-    };
-#pragma unroll
-    for (int p = 0; p < kXPre; ++p) {
-        const int e = tid + p * kFThreads;
-        if (e < ng) stage(xr[p], e);
-    }
-    for (int e = tid + kXPre * kFThreads; e < ng; e += kFThreads) {
-        const int m = e / gpc, g = e - m * gpc;
-        const uint4 *src = reinterpret_cast<const uint4 *>(xbase + (size_t)(m0 + m) * K * gsz) +
-                           (size_t)g * gsz;
-        uint4 raw[4];
-        raw[0] = src[0];
-        raw[1] = src[1];
-        if (dtype == 0) { raw[2] = src[2]; raw[3] = src[3]; }
-        stage(raw, e);
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            amax[m] = fmaxf(amax[m], __shfl_xor(amax[m], off));
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) red[tid >> 6][m] = amax[m];
-    }
-    __syncthreads();
-    const bool writer = (wg == 0);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        float a = red[0][m];
-#pragma unroll
-        for (int v = 1; v < kFThreads / 64; ++v) a = fmaxf(a, red[v][m]);
-        if (m < mt) {
-            const float sc = act_inv_scale(a);
-            for (int g = tid; g < gpc; g += kFThreads) {
-                uint4 raw[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    if (t < gsz) raw[t] = xraw[((size_t)m * gpc + g) * gsz + t];
-                float x[16];
-                unpack_x16(raw, dtype, x);
-                uint32_t q4[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    q4[t] = (uint32_t)(act_code(x[4 * t], sc) & 0xFF) |
-                            ((uint32_t)(act_code(x[4 * t + 1], sc) & 0xFF) << 8) |
-                            ((uint32_t)(act_code(x[4 * t + 2], sc) & 0xFF) << 16) |
-                            ((uint32_t)(act_code(x[4 * t + 3], sc) & 0xFF) << 24);
-                const uint4 qv = make_uint4(q4[0], q4[1], q4[2], q4[3]);
-                if (writer && jb.Xq)
-                    *reinterpret_cast<uint4 *>(jb.Xq + (size_t)(m0 + m) * K + 16 * g) = qv;
-                xs[m * gpc + g] = transpose16(qv);
-            }
-            if (writer && jb.d && tid == 0)
-                jb.d[m0 + m] = act_scale(a);
-        }
-    }
-    __syncthreads();
+        w[q] = ld_stream(wrow + min(sig + q * L, U - 1));  // a job with N == 0 reads its own X here
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    while (__hip_atomic_load(&n_codes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kQWaves)
+        __builtin_amdgcn_s_sleep(1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
     if constexpr (kMfma) {
-        // 3. dot products on MFMA over the lane's units; slots past the
-        //    row's last unit take zero weights (the loop is wave-uniform)
+        // dot products on MFMA over the lane's units; slots past the row's
+        // last unit take zero weights (the loop is wave-uniform)
         static_assert(MT == 1, "the MFMA mapping carries one token");
         const int nslot = (U + L - 1) / L;
         v4i acc4 = v4i{0, 0, 0, 0};
@@ -447,19 +466,19 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         }
         // lane i < 16: D[i % c][i], then the sum over the row's c columns
         const int c = L >> 2;
-        const int j = lane % c;
-        int v = j == 0 ? acc4[0] : j == 1 ? acc4[1] : j == 2 ? acc4[2] : acc4[3];
+        const int jc = lane % c;
+        int v = jc == 0 ? acc4[0] : jc == 1 ? acc4[1] : jc == 2 ? acc4[2] : acc4[3];
         for (int off = c >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        if (lane < 16 && j == 0 && row < N) {
+        if (lane < 16 && jc == 0 && row < N) {
             float a = red[0][0];
 #pragma unroll
-            for (int vv = 1; vv < kFThreads / 64; ++vv) a = fmaxf(a, red[vv][0]);
+            for (int vv = 1; vv < kQWaves; ++vv) a = fmaxf(a, red[vv][0]);
             jb.Y[(size_t)m0 * N + row] = rescale(v, __fmul_rn(gam, act_scale(a)));
         }
         return;
     }
 
-    // 3. dot products over this lane's units, software-pipelined
+    // dot products over this lane's units, software-pipelined
     int acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0;
@@ -492,7 +511,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         for (int m = 0; m < MT; ++m) {
             float a = red[0][m];
 #pragma unroll
-            for (int v = 1; v < kFThreads / 64; ++v) a = fmaxf(a, red[v][m]);
+            for (int v = 1; v < kQWaves; ++v) a = fmaxf(a, red[v][m]);
             dm[m] = act_scale(a);
         }
 #pragma unroll
@@ -553,7 +572,7 @@ hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t 
 #ifdef BL_FUSED_LSHIFT
         f.lshift = BL_FUSED_LSHIFT;                     // tuning builds only
 #endif
-        const int rows_per_wg = (kFThreads / 64) * (64 >> f.lshift);
+        const int rows_per_wg = (kCThreads / 64) * (64 >> f.lshift);
         f.wg_begin = wg;
         // a job with N == 0 still gets one workgroup when it must write Xq / d
         const int n_wg = f.N > 0 ? (f.N + rows_per_wg - 1) / rows_per_wg : ((f.Xq || f.d) ? 1 : 0);
