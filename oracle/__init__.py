@@ -55,6 +55,12 @@ def _load():
     lib.ob_bf16_to_f32.argtypes = [_p, _i64, _p]
     lib.ob_quant_act.restype = None
     lib.ob_quant_act.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.ob_quant_act4.restype = None
+    lib.ob_quant_act4.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.ob_pack_act4.restype = None
+    lib.ob_pack_act4.argtypes = [_p, _i64, _i64, _p]
+    lib.ob_unpack_act4.restype = None
+    lib.ob_unpack_act4.argtypes = [_p, _i64, _i64, _p]
     lib.ob_ternary_acc.restype = None
     lib.ob_ternary_acc.argtypes = [_p, _p, _i64, _i64, _i64, _p]
     lib.ob_dequant_f64.restype = None
@@ -180,6 +186,46 @@ def quant_act(X):
     d = np.empty((M,), dtype=np.float32)
     _load().ob_quant_act(_ptr(X), M, K, _ptr(Xq), _ptr(d))
     return Xq, d
+
+
+def quant_act4(X):
+    """Per-token absmax to signed 4-bit codes: X float32 [M, K] ->
+    (codes int8 [M, K] in [-7, 7], d float32 [M])."""
+    X = _c(X, np.float32)
+    M, K = X.shape
+    Xq = np.empty((M, K), dtype=np.int8)
+    d = np.empty((M,), dtype=np.float32)
+    _load().ob_quant_act4(_ptr(X), M, K, _ptr(Xq), _ptr(d))
+    return Xq, d
+
+
+def pack_act4(Xq):
+    """int8 codes [M, K] (K even) -> two per byte, uint8 [M, K/2]."""
+    Xq = _c(Xq, np.int8)
+    M, K = Xq.shape
+    if K % 2:
+        raise ValueError("K must be even")
+    out = np.empty((M, K // 2), dtype=np.uint8)
+    _load().ob_pack_act4(_ptr(Xq), M, K, _ptr(out))
+    return out
+
+
+def unpack_act4(P, K):
+    """uint8 [M, K/2] -> int8 codes [M, K] in [-8, 7]."""
+    P = _c(P, np.uint8)
+    M = P.shape[0]
+    if P.shape[1] * 2 != K:
+        raise ValueError("shape mismatch")
+    out = np.empty((M, K), dtype=np.int8)
+    _load().ob_unpack_act4(_ptr(P), M, K, _ptr(out))
+    return out
+
+
+def bitlinear_a4(P, d, Wp, gamma, K):
+    """One BitLinear from 4-bit packed activation codes: (acc int32 [M, N],
+    Y float64 [M, N]); the codes are unpacked, then the product and rescale
+    are those of the 8-bit codes."""
+    return bitlinear(unpack_act4(P, K), d, Wp, gamma, K)
 
 
 def ternary_acc(Xq, Wp, K):

@@ -244,6 +244,72 @@ OB_EXPORT void ob_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, fl
     }
 }
 
+/* "Microsoft BitNet 深度研究报告", §3 论文演进时间线 (the BitNet a4.8 row:
+ * activations at 4 bits, a further compression) and §10 关键资源 (BitNet
+ * a4.8, activation quantisation).  The pages name the 4-bit activations and
+ * nothing else.  Reading taken: the absmax rule of ob_quant_act with the
+ * signed 4-bit range, for each token row m:
+ *     a   = max_k |x[m][k]|
+ *     s   = fl32(7 / a)
+ *     q   = clamp(rne(fl32(x * s)), -7, 7)
+ *     d   = fl32(a / 7)                          (x ~= q * d)
+ * an all-zero row giving q = 0, d = 0 (-8 is never produced).  The codes go
+ * into the same ternary accumulation and rescale as the 8-bit ones. */
+OB_EXPORT void ob_quant_act4(const float *X, int64_t M, int64_t K, int8_t *Xq, float *d)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const float *x = X + m * K;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float ax = fabsf(x[k]);
+            if (ax > a) a = ax;
+        }
+        if (a == 0.0f) {
+            for (int64_t k = 0; k < K; ++k) Xq[m * K + k] = 0;
+            d[m] = 0.0f;
+            continue;
+        }
+        float s = 7.0f / a;
+        for (int64_t k = 0; k < K; ++k) {
+            float p = x[k] * s;
+            float r = nearbyintf(p);
+            if (r > 7.0f) r = 7.0f;
+            if (r < -7.0f) r = -7.0f;
+            Xq[m * K + k] = (int8_t)r;
+        }
+        d[m] = a / 7.0f;
+    }
+}
+
+/* Storage of the 4-bit codes (the pages give none).  Reading taken: two
+ * codes per byte, row-major [M][K/2]; byte b of a row holds element 2b in
+ * bits 0..3 and element 2b+1 in bits 4..7, each as a 4-bit two's-complement
+ * number.  K must be even. */
+OB_EXPORT void ob_pack_act4(const int8_t *Xq, int64_t M, int64_t K, uint8_t *P)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < K / 2; ++b) {
+            uint8_t lo = (uint8_t)Xq[m * K + 2 * b] & 0x0F;
+            uint8_t hi = (uint8_t)Xq[m * K + 2 * b + 1] & 0x0F;
+            P[m * (K / 2) + b] = (uint8_t)(lo | (hi << 4));
+        }
+}
+
+static int8_t ob_nibble(uint8_t v)               /* 4-bit two's complement */
+{
+    return (int8_t)(v < 8 ? v : (int)v - 16);
+}
+
+OB_EXPORT void ob_unpack_act4(const uint8_t *P, int64_t M, int64_t K, int8_t *Xq)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < K / 2; ++b) {
+            uint8_t v = P[m * (K / 2) + b];
+            Xq[m * K + 2 * b] = ob_nibble(v & 0x0F);
+            Xq[m * K + 2 * b + 1] = ob_nibble(v >> 4);
+        }
+}
+
 /* [RPT] §2 (3) 查找表优化: with W in {-1, 0, +1}, C = A x Q(W) needs no
  * multiplication:  W = +1: C += A;  W = -1: C -= A;  W = 0: skip.
  *

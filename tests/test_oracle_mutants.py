@@ -63,6 +63,14 @@ MUTANTS = [
     ("ffn_rms_no_mean", "sqrt(ss / (double)F + (double)eps)", "sqrt(ss + (double)eps)"),
     ("ffn_gain_dropped", "float z = norm_w ? h * norm_w[f] : h;", "float z = h;"),
     ("ffn_y32_scale_order", "float c = gamma_d * dz32;", "float c = gamma_d * (float)dh[m];"),
+    ("act4_8_levels", "float s = 7.0f / a;", "float s = 8.0f / a;"),
+    ("act4_clamp_6", "if (r > 7.0f) r = 7.0f;", "if (r > 6.0f) r = 6.0f;"),
+    ("act4_scale_wrong", "d[m] = a / 7.0f;", "d[m] = a / 8.0f;"),
+    ("act4_trunc", "            float r = nearbyintf(p);\n            if (r > 7.0f)",
+     "            float r = truncf(p);\n            if (r > 7.0f)"),
+    ("act4_nibble_order", "P[m * (K / 2) + b] = (uint8_t)(lo | (hi << 4));",
+     "P[m * (K / 2) + b] = (uint8_t)(hi | (lo << 4));"),
+    ("act4_unsigned_nibble", "return (int8_t)(v < 8 ? v : (int)v - 16);", "return (int8_t)v;"),
 ]
 
 
@@ -78,7 +86,8 @@ def _run_mutant(name, old, new, src_text, tmpdir):
     env = dict(os.environ, BITLINEAR_ORACLE_LIB=mut_so, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(HERE, "test_oracle_pins.py"),
-                        os.path.join(HERE, "test_oracle_stack.py")],
+                        os.path.join(HERE, "test_oracle_stack.py"),
+                        os.path.join(HERE, "test_oracle_a4.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-400:]
 
