@@ -87,7 +87,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--part", default="all",
                     choices=["all", "decode", "batched", "gemm", "ffn", "stack", "qat", "t5",
-                             "copy"],
+                             "a4", "copy"],
                     help="restrict the GPU legs (for profiling runs); 'copy' (not in 'all') "
                          "times a plain device copy of 256 MiB, the reference for the "
                          "byte counters")
@@ -496,6 +496,70 @@ def bench_t5(bl, torch, workloads, steps, warmup):
     return out
 
 
+def bench_a4(bl, torch, workloads, steps, warmup):
+    """4-bit activations (BitNet a4.8) against 8-bit: the decode step's four
+    products at M = 1 from pre-quantised tokens, as four bitlinear_a4 and as
+    four bitlinear_gemv launches, weights rotated over copies past the
+    Infinity Cache, replayed from HIP graphs; and the prefill product at
+    M = 2048, K2560 -> N6912, bitlinear_a4 against bitlinear_gemm.  GB/s and
+    TOPS count each format's own bytes and 2 M N K."""
+    shapes = workloads.DECODE_SHAPES
+    base = []
+    for i, s in enumerate(shapes):
+        W, X = workloads.bitlinear_problem(i, 1, s.K, s.N)
+        Wp, g = bl.quant_weight_absmean_pack(W.cuda())
+        Xq, d = bl.quant_act_absmax_i8(X.cuda())
+        P, d4 = bl.quant_act_absmax_i4(X.cuda())
+        base.append(dict(shape=s, Wp=Wp, g=g, Xq=Xq, d=d, P=P, d4=d4,
+                         Y=torch.empty((1, s.N), dtype=torch.float32, device="cuda")))
+    per_step = sum(p["Wp"].numel() for p in base)
+    reps = STEPS_PER_GRAPH * math.ceil(max(2, math.ceil(COLD_BYTES / per_step)) / STEPS_PER_GRAPH)
+    copies = [[p["Wp"]] + [p["Wp"].clone() for _ in range(reps - 1)] for p in base]
+    out = {}
+    for name, xk, dk, call, abytes in (("a8", "Xq", "d", bl.bitlinear_gemv, 1.0),
+                                       ("a4", "P", "d4", bl.bitlinear_a4, 0.5)):
+        def step(r):
+            for p, c in zip(base, copies):
+                call(p[xk], p[dk], c[r], p["g"], Y=p["Y"])
+        for r in range(reps):
+            step(r)
+        torch.cuda.synchronize()
+        graphs = capture(torch, step, reps, STEPS_PER_GRAPH)
+        ms = replay_ms(torch, graphs, steps, warmup, STEPS_PER_GRAPH)
+        us = 1000.0 * ms / steps
+        nbytes = per_step + sum(int(abytes * p["shape"].K) + 4 * p["shape"].N + 8 for p in base)
+        out[name] = dict(us_per_step=round(us, 3), step_bytes=nbytes, GBs=round(nbytes / us / 1e3, 1),
+                         launches_per_step=len(base))
+        del graphs
+    del copies
+    p = workloads.PREFILL
+    M, K, N = p["M"], p["K"], p["F"]
+    W, X = workloads.bitlinear_problem(p["seed"], M, K, N)
+    Wp, g = bl.quant_weight_absmean_pack(W.cuda())
+    Xq, d = bl.quant_act_absmax_i8(X.cuda())
+    P4, d4 = bl.quant_act_absmax_i4(X.cuda())
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pre = {}
+    for name, fn in (("a8", lambda: bl.bitlinear_gemm(Xq, d, Wp, g, Y=Y)),
+                     ("a4", lambda: bl.bitlinear_a4(P4, d4, Wp, g, Y=Y))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        n = max(10, steps // 8)
+        t0.record()
+        for _ in range(n):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * t0.elapsed_time(t1) / n
+        tops = 2.0 * M * N * K / us / 1e6
+        pre[name] = dict(us=round(us, 2), TOPS=round(tops, 1), frac=round(tops / I8_MFMA_PEAK_TOPS, 4))
+    out["prefill_M2048_K2560_N6912"] = pre
+    return out
+
+
 def bench_copy(torch, steps):
     """A plain device-to-device copy of 256 MiB: the kernel whose HBM byte
     counters (FETCH_SIZE, WRITE_SIZE) calibrate the ones read for the GEMV."""
@@ -711,6 +775,8 @@ def main():
         out["qat_backward"] = bench_qat(bl, torch, workloads, max(5, args.steps // 40), 2)
     if args.part in ("all", "t5"):
         out["t5_storage"] = bench_t5(bl, torch, workloads, max(20, args.steps // 2), 10)
+    if args.part in ("all", "a4"):
+        out["a4_activations"] = bench_a4(bl, torch, workloads, max(20, args.steps // 2), 10)
     if args.part == "copy":
         out["copy"] = bench_copy(torch, 10)
     if args.part in ("all", "stack"):

@@ -150,6 +150,34 @@ bl_status quant_act_absmax_i8(const void *X, bl_dtype dtype, int64_t M, int64_t 
                               int8_t *Xq, float *d, void *stream);
 
 /* ------------------------------------------------------------------------
+ * 4-bit activations (BitNet a4.8): "Microsoft BitNet 深度研究报告",
+ * §3 论文演进时间线 (row 2024-11: activations at 4 bits, a further
+ * compression) and §10 关键资源 (BitNet a4.8, activation quantisation).
+ * The pages name the scheme only.  Readings: the per-token absmax rule above
+ * with the signed 4-bit range,
+ *     s = fp32(7 / a),  q = clamp(rne(fp32(x * s)), -7, 7),  d = fp32(a / 7),
+ * an all-zero row giving q = 0, d = 0 (-8 is never produced); storage Xq4:
+ * uint8 [M][K/2] row-major, byte b holding element 2b in bits 0..3 and
+ * element 2b+1 in bits 4..7, each a 4-bit two's-complement number; the
+ * product and rescale are those of the 8-bit codes:
+ *     acc = sum_k q[m][k] * Wq[n][k] (exact int32),  Y = fp32(float(acc) * fp32(gamma * d[m])).
+ *
+ * quant_act_absmax_i4 -- X [M][K] fp32 or bf16 (16-byte aligned), K even,
+ *   K <= BL_MAX_K -> Xq4 [M][K/2] (16-byte aligned) and d [M].  Bit-exact.
+ */
+bl_status quant_act_absmax_i4(const void *X, bl_dtype dtype, int64_t M, int64_t K,
+                              uint8_t *Xq4, float *d, void *stream);
+
+/* bitlinear_a4 -- the W1.58A4 product for any M >= 0: arguments, formats and
+ * errors as bitlinear_gemm, with Xq4 [M][K/2] (16-byte aligned) in place of
+ * Xq; K % 64 == 0.  The 4-bit codes are unpacked into the same int8 product
+ * kernels (the decode kernel for M <= 8, the int8 MFMA tiles above), so acc
+ * and Y are bit-exact. */
+bl_status bitlinear_a4(const uint8_t *Xq4, const float *d, int64_t M,
+                       const uint8_t *Wp, const float *gamma, int64_t N, int64_t K,
+                       float *Y, int32_t *acc, void *stream);
+
+/* ------------------------------------------------------------------------
  * bitlinear_gemv -- decode-sized W1.58A8 product, M = 1..64 tokens.
  * [RPT] §2 (3) 查找表优化 (add / subtract / skip); [TR] GPU端 (load the
  * packed weights, unpack, compute); [CARD] 模型详情 (W1.58A8).

@@ -9,7 +9,8 @@ from ._native import (  # noqa: F401
     BL_OP_DECODE_STACK, BL_OP_FFN_RELU2, BL_OP_QUANT_WEIGHT, BL_STACK_AUTO, BL_STACK_LAUNCHES,
     BL_STACK_PERSISTENT, EXPORTS, LAYER_GAMMAS, LAYER_WEIGHTS, LIB_PATH, BitLinearError,
     GemvJob, Layer, StackDims, bitlinear_backward_input, bitlinear_backward_weight,
-    bitlinear_decode_stack, bitlinear_decode_stack_status, bitlinear_ffn_relu2, bitlinear_gemm, bitlinear_gemv,
-    bitlinear_gemv_fused, bitlinear_gemv_t5, bitlinear_repack_t5, load, quant_act_absmax_i8,
+    bitlinear_a4, bitlinear_decode_stack, bitlinear_decode_stack_status, bitlinear_ffn_relu2, bitlinear_gemm, bitlinear_gemv,
+    bitlinear_gemv_fused, bitlinear_gemv_t5, bitlinear_repack_t5, load, quant_act_absmax_i4,
+    quant_act_absmax_i8,
     quant_weight_absmean_pack, quant_weight_absmean_pack_noalloc, t5_row_bytes, workspace_bytes,
 )

@@ -24,7 +24,8 @@ BL_MAX_K = 131072
 STATUS = {0: "BL_OK", 1: "BL_ERR_NULL", 2: "BL_ERR_SHAPE", 3: "BL_ERR_DTYPE",
           4: "BL_ERR_ALIGN", 5: "BL_ERR_WORKSPACE", 6: "BL_ERR_ARCH", 7: "BL_ERR_HIP"}
 
-EXPORTS = ["quant_weight_absmean_pack", "quant_weight_absmean_pack_noalloc", "quant_act_absmax_i8", "bitlinear_gemv",
+EXPORTS = ["quant_weight_absmean_pack", "quant_weight_absmean_pack_noalloc", "quant_act_absmax_i8",
+           "quant_act_absmax_i4", "bitlinear_a4", "bitlinear_gemv",
            "bitlinear_gemm", "bitlinear_gemv_fused", "bitlinear_ffn_relu2",
            "bitlinear_decode_stack", "bitlinear_decode_stack_status",
            "bitlinear_backward_input", "bitlinear_backward_weight",
@@ -90,7 +91,9 @@ def load():
     lib.quant_weight_absmean_pack_noalloc.argtypes = [_p, _i64, _i64, _p, _p, _p]
     lib.quant_act_absmax_i8.restype = st
     lib.quant_act_absmax_i8.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p]
-    for name in ("bitlinear_gemv", "bitlinear_gemm"):
+    lib.quant_act_absmax_i4.restype = st
+    lib.quant_act_absmax_i4.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p]
+    for name in ("bitlinear_gemv", "bitlinear_gemm", "bitlinear_a4"):
         f = getattr(lib, name)
         f.restype = st
         f.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _p]
@@ -210,12 +213,14 @@ def quant_act_absmax_i8(X, Xq=None, d=None, stream=None):
     return Xq, d
 
 
-def _product(call, Xq, d, Wp, gamma, Y, acc, want_acc, stream):
-    _dev(Xq, torch.int8, "Xq")
+def _product(call, Xq, d, Wp, gamma, Y, acc, want_acc, stream, a4=False):
+    _dev(Xq, torch.uint8 if a4 else torch.int8, "Xq4" if a4 else "Xq")
     _dev(d, torch.float32, "d")
     _dev(Wp, torch.uint8, "Wp")
     _dev(gamma, torch.float32, "gamma")
     M, K = Xq.shape
+    if a4:
+        K *= 2
     N = Wp.shape[0]
     if Wp.dim() != 2 or Wp.shape[1] * 4 != K:
         raise ValueError(f"Wp must be [N, K/4] = [*, {K // 4}], got {tuple(Wp.shape)}")
@@ -239,6 +244,31 @@ def bitlinear_gemv(Xq, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=No
 def bitlinear_gemm(Xq, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=None):
     """Y [M, N] fp32 for any M on int8 MFMA; with want_acc also int32 acc."""
     return _product("bitlinear_gemm", Xq, d, Wp, gamma, Y, acc, want_acc, stream)
+
+
+def quant_act_absmax_i4(X, Xq4=None, d=None, stream=None):
+    """X [M, K] (fp32 or bf16, K even) -> (Xq4 uint8 [M, K/2] 4-bit codes, d fp32 [M])."""
+    if X.dtype == torch.float32:
+        dt = BL_F32
+    elif X.dtype == torch.bfloat16:
+        dt = BL_BF16
+    else:
+        raise TypeError("X must be float32 or bfloat16")
+    _dev(X, X.dtype, "X")
+    M, K = X.shape
+    Xq4 = _dev(Xq4, torch.uint8, "Xq4") if Xq4 is not None else torch.empty(
+        (M, K // 2), dtype=torch.uint8, device=X.device)
+    d = _dev(d, torch.float32, "d") if d is not None else torch.empty(
+        (M,), dtype=torch.float32, device=X.device)
+    _check("quant_act_absmax_i4", load().quant_act_absmax_i4(
+        _ptr(X), dt, M, K, _ptr(Xq4), _ptr(d), _stream(stream)))
+    return Xq4, d
+
+
+def bitlinear_a4(Xq4, d, Wp, gamma, Y=None, acc=None, want_acc=False, stream=None):
+    """Y [M, N] fp32 from 4-bit activation codes Xq4 uint8 [M, K/2]; with
+    want_acc also the int32 accumulator."""
+    return _product("bitlinear_a4", Xq4, d, Wp, gamma, Y, acc, want_acc, stream, a4=True)
 
 
 def t5_row_bytes(K):

@@ -261,6 +261,42 @@ BL_EXPORT bl_status quant_act_absmax_i8(const void *X, bl_dtype dtype, int64_t M
                     name);
 }
 
+BL_EXPORT bl_status quant_act_absmax_i4(const void *X, bl_dtype dtype, int64_t M, int64_t K,
+                                        uint8_t *Xq4, float *d, void *stream) {
+    const char *name = "quant_act_absmax_i4";
+    if (M < 0 || K < 0 || K % 2 != 0 || K > BL_MAX_K || M > kI32Max)
+        return fail(BL_ERR_SHAPE, "%s: need M in [0, 2^31), K in [0, %d] and even (M=%lld K=%lld)",
+                    name, BL_MAX_K, (long long)M, (long long)K);
+    if (dtype != BL_F32 && dtype != BL_BF16)
+        return fail(BL_ERR_DTYPE, "%s: unknown dtype %d", name, (int)dtype);
+    if (M == 0)
+        return ok();
+    if (!d || (K > 0 && (!X || !Xq4)))
+        return fail(BL_ERR_NULL, "%s: NULL pointer (X=%p Xq4=%p d=%p)", name, X, (void *)Xq4,
+                    (void *)d);
+    if ((K > 0 && (!aligned(X, 16) || !aligned(Xq4, 16))) || !aligned(d, 4))
+        return fail(BL_ERR_ALIGN, "%s: X and Xq4 must be 16-byte aligned, d 4-byte", name);
+    bl_status st = check_arch();
+    if (st != BL_OK)
+        return st;
+    return launched(bl::launch_quant_act4(X, dtype == BL_BF16 ? 1 : 0, M, K, Xq4, d,
+                                          static_cast<hipStream_t>(stream)),
+                    name);
+}
+
+BL_EXPORT bl_status bitlinear_a4(const uint8_t *Xq4, const float *d, int64_t M, const uint8_t *Wp,
+                                 const float *gamma, int64_t N, int64_t K, float *Y, int32_t *acc,
+                                 void *stream) {
+    bool noop = false;
+    bl_status st = check_product("bitlinear_a4", reinterpret_cast<const int8_t *>(Xq4), d, M,
+                                 kI32Max, Wp, gamma, N, K, Y, acc, &noop);
+    if (st != BL_OK || noop)
+        return st;
+    return launched(bl::launch_bitlinear_a4(Xq4, d, (int)M, Wp, gamma, (int)N, (int)K, Y, acc,
+                                            static_cast<hipStream_t>(stream)),
+                    "bitlinear_a4");
+}
+
 BL_EXPORT bl_status bitlinear_gemv(const int8_t *Xq, const float *d, int64_t M, const uint8_t *Wp,
                                    const float *gamma, int64_t N, int64_t K, float *Y,
                                    int32_t *acc, void *stream) {

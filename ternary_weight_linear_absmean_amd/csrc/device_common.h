@@ -62,6 +62,26 @@ __device__ __forceinline__ uint4 transpose16(uint4 v) {
     return o;
 }
 
+// Sixteen 4-bit activation codes (8 bytes; element 2b in bits 0..3 of byte b,
+// element 2b+1 in bits 4..7, 4-bit two's complement) -> their int8 values in
+// the order transpose16 gives: dword i holds elements {i, 4+i, 8+i, 12+i}.
+// The low and high nibbles are split into bytes, picked into place with
+// v_perm, and each byte n is sign-extended as ((n ^ 8) + 0x78) ^ 0x80, which
+// never carries into the next byte.
+__device__ __forceinline__ uint32_t sext4_bytes(uint32_t v) {
+    return ((v ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+}
+__device__ __forceinline__ uint4 a4_to_t16(uint2 p) {
+    const uint32_t lx = p.x & 0x0F0F0F0Fu, hx = (p.x >> 4) & 0x0F0F0F0Fu;   // e0 e2 e4 e6 | e1 e3 e5 e7
+    const uint32_t ly = p.y & 0x0F0F0F0Fu, hy = (p.y >> 4) & 0x0F0F0F0Fu;   // e8 .. e14  | e9 .. e15
+    uint4 t;
+    t.x = sext4_bytes(perm(ly, lx, 0x06040200u));                           // e0 e4 e8 e12
+    t.y = sext4_bytes(perm(hy, hx, 0x06040200u));                           // e1 e5 e9 e13
+    t.z = sext4_bytes(perm(ly, lx, 0x07050301u));                           // e2 e6 e10 e14
+    t.w = sext4_bytes(perm(hy, hx, 0x07050301u));                           // e3 e7 e11 e15
+    return t;
+}
+
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
@@ -85,6 +105,20 @@ __device__ __forceinline__ float act_scale(float a) {
 __device__ __forceinline__ int act_code(float x, float s) {
     float r = __builtin_rintf(__fmul_rn(x, s));
     r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// The same rule at 4 bits ("Microsoft BitNet 深度研究报告", §3 论文演进时间线:
+// BitNet a4.8): s = fl(7 / a), q = clamp(rne(fl(x * s)), -7, 7), d = fl(a / 7).
+__device__ __forceinline__ float act4_inv_scale(float a) {
+    return a > 0.0f ? __fdiv_rn(7.0f, a) : 0.0f;
+}
+__device__ __forceinline__ float act4_scale(float a) {
+    return a > 0.0f ? __fdiv_rn(a, 7.0f) : 0.0f;
+}
+__device__ __forceinline__ int act4_code(float x, float s) {
+    float r = __builtin_rintf(__fmul_rn(x, s));
+    r = fminf(fmaxf(r, -7.0f), 7.0f);
     return (int)r;
 }
 

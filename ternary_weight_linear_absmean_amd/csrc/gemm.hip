@@ -32,6 +32,10 @@ __device__ __forceinline__ v4i as_v4i(uint4 v) {
     return r;
 }
 
+// A4: the activations are 4-bit codes, two per byte ([M][K/2]); only the
+// staging differs (eight bytes per 16-element group, sign-extended into the
+// same transposed int8 group).
+template <bool A4>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
@@ -61,10 +65,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(
             const int r = idx >> 2;
             const int g = idx & 3;
             const int gm = m_base + r;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (gm < M)
-                v = *reinterpret_cast<const uint4 *>(Xq + (size_t)gm * K + k0 + 16 * g);
-            As[r * kPitch + g] = transpose16(v);
+            if constexpr (A4) {
+                uint2 v = make_uint2(0u, 0u);
+                if (gm < M)
+                    v = *reinterpret_cast<const uint2 *>(Xq + ((size_t)gm * K + k0 + 16 * g) / 2);
+                As[r * kPitch + g] = a4_to_t16(v);
+            } else {
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (gm < M)
+                    v = *reinterpret_cast<const uint4 *>(Xq + (size_t)gm * K + k0 + 16 * g);
+                As[r * kPitch + g] = transpose16(v);
+            }
         }
         if (tid < BN) {
             const int gn = n_base + tid;
@@ -151,7 +162,9 @@ template <int AG, int BG> struct SrcPtr { const int8_t *a[AG]; const uint8_t *b[
 // Per k-step a workgroup of T threads stages BM rows x 128 bytes of A (BM * 8
 // groups of 16 bytes, AG = BM * 8 / T per thread) and BN columns x 32 packed
 // bytes of B (BN * 2 groups of 16 bytes, BG = BN * 2 / T per thread).
-template <int BM, int BN, int T, int AG, int BG>
+// With A4 the activation rows are 4-bit codes, K / 2 bytes each, and a
+// 16-element group is 8 bytes.
+template <int BM, int BN, int T, int AG, int BG, bool A4>
 __device__ __forceinline__ SrcPtr<AG, BG> src_ptrs(const int8_t *__restrict__ Xq,
         const uint8_t *__restrict__ Wp, int M, int N, int K, int KB, int m_base, int n_base, int tid) {
     SrcPtr<AG, BG> p;
@@ -159,7 +172,7 @@ __device__ __forceinline__ SrcPtr<AG, BG> src_ptrs(const int8_t *__restrict__ Xq
     for (int i = 0; i < AG; ++i) {
         const int idx = tid + T * i;
         const int r = min(m_base + (idx >> 3), M - 1);
-        p.a[i] = Xq + (size_t)r * K + 16 * (idx & 7);
+        p.a[i] = A4 ? Xq + ((size_t)r * K + 16 * (idx & 7)) / 2 : Xq + (size_t)r * K + 16 * (idx & 7);
     }
 #pragma unroll
     for (int i = 0; i < BG; ++i) {
@@ -199,19 +212,27 @@ __device__ __forceinline__ void gate_up_b_ptrs(SrcPtr<AG, BG> &p, const uint8_t 
     }
 }
 
-template <int AG, int BG>
+template <int AG, int BG, bool A4>
 __device__ __forceinline__ void load_stage2(Stage2<AG, BG> &st, const SrcPtr<AG, BG> &sp, int k0) {
 #pragma unroll
-    for (int i = 0; i < AG; ++i) st.a[i] = *reinterpret_cast<const uint4 *>(sp.a[i] + k0);
+    for (int i = 0; i < AG; ++i) {
+        if constexpr (A4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(sp.a[i] + k0 / 2);
+            st.a[i] = make_uint4(v.x, v.y, 0u, 0u);
+        } else {
+            st.a[i] = *reinterpret_cast<const uint4 *>(sp.a[i] + k0);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < BG; ++i) st.b[i] = *reinterpret_cast<const uint4 *>(sp.b[i] + k0 / 4);
 }
-template <int T, int AG, int BG>
+template <int T, int AG, int BG, bool A4>
 __device__ __forceinline__ void store_stage2(const Stage2<AG, BG> &st, uint4 *As, uint32_t *Bs, int tid) {
 #pragma unroll
     for (int i = 0; i < AG; ++i) {
         const int idx = tid + T * i;
-        As[(idx >> 3) * kAPitch + (idx & 7)] = transpose16(st.a[i]);
+        As[(idx >> 3) * kAPitch + (idx & 7)] =
+            A4 ? a4_to_t16(make_uint2(st.a[i].x, st.a[i].y)) : transpose16(st.a[i]);
     }
 #pragma unroll
     for (int i = 0; i < BG; ++i) {
@@ -286,7 +307,7 @@ __device__ __forceinline__ void gate_up_epilogue(const v16i (&acc)[MI2][2], floa
     }
 }
 
-template <int WM, int WN, int MI2, int NJ2, bool GU>
+template <int WM, int WN, int MI2, int NJ2, bool GU, bool A4 = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
@@ -325,7 +346,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     for (int i = 0; i < MI2; ++i)
 #pragma unroll
         for (int j = 0; j < NJ2; ++j) acc[i][j] = v16i{};
-    SrcPtr<AG, BG> sp = src_ptrs<BM2, BN2, kThreads2, AG, BG>(Xq, Wp, M, N, K, KB, m_base, n_base, tid);
+    SrcPtr<AG, BG> sp = src_ptrs<BM2, BN2, kThreads2, AG, BG, A4>(Xq, Wp, M, N, K, KB, m_base, n_base, tid);
     if constexpr (GU) gate_up_b_ptrs<BN2, kThreads2, AG, BG>(sp, Wp, gu.Wu, N, KB, n_base, tid);
     const int a_off = (wm * 32 * MI2 + (lane & 31)) * kAPitch + (lane >> 5);
     const int b_off = (wn * 32 * NJ2 + (lane & 31)) * kBPitch + (lane >> 5);
@@ -354,15 +375,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
     const int kt_last = KT - 1;
     if (KT > 0) {
         Stage2<AG, BG> s0, s1;
-        load_stage2(s0, sp, 0);
-        load_stage2(s1, sp, min(1, kt_last) * BK2);
+        load_stage2<AG, BG, A4>(s0, sp, 0);
+        load_stage2<AG, BG, A4>(s1, sp, min(1, kt_last) * BK2);
         put_row_factors();
-        store_stage2<kThreads2>(s0, As, Bs, tid);
+        store_stage2<kThreads2, AG, BG, A4>(s0, As, Bs, tid);
         __syncthreads();
 #define BL_STEP(KT_, MINE, NEXT)                                                              \
         {                                                                                         \
             const int kt_ = (KT_);                                                                \
-            load_stage2(MINE, sp, min(kt_ + 2, kt_last) * BK2);                                   \
+            load_stage2<AG, BG, A4>(MINE, sp, min(kt_ + 2, kt_last) * BK2);                      \
             const int buf = kt_ & 1;                                                              \
             __builtin_amdgcn_iglp_opt(1);                                                       \
             const uint4 *A = As + buf * kStageA + a_off;                                          \
@@ -383,7 +404,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0); \
                 if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);                              \
             }                                                                                     \
-            if (kt_ + 1 < KT) store_stage2<kThreads2>(NEXT, As + (buf ^ 1) * kStageA, Bs + (buf ^ 1) * kStageB, tid); \
+            if (kt_ + 1 < KT) store_stage2<kThreads2, AG, BG, A4>(NEXT, As + (buf ^ 1) * kStageA, Bs + (buf ^ 1) * kStageB, tid); \
             __syncthreads();                                                                      \
         }
         int kt = 0;
@@ -406,14 +427,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
 #pragma unroll
         for (int i = 0; i < AG; ++i) {
             const int idx = tid + kThreads2 * i;
-            st.a[i] = (idx & 7) < 4 ? *reinterpret_cast<const uint4 *>(sp.a[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (A4) {
+                uint2 v = make_uint2(0u, 0u);
+                if ((idx & 7) < 4) v = *reinterpret_cast<const uint2 *>(sp.a[i] + k0 / 2);
+                st.a[i] = make_uint4(v.x, v.y, 0u, 0u);
+            } else {
+                st.a[i] = (idx & 7) < 4 ? *reinterpret_cast<const uint4 *>(sp.a[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
 #pragma unroll
         for (int i = 0; i < BG; ++i) {
             const int idx = tid + kThreads2 * i;
             st.b[i] = (idx & 1) == 0 ? *reinterpret_cast<const uint4 *>(sp.b[i] + k0 / 4) : make_uint4(0u, 0u, 0u, 0u);
         }
-        store_stage2<kThreads2>(st, As, Bs, tid);
+        store_stage2<kThreads2, AG, BG, A4>(st, As, Bs, tid);
         __syncthreads();
         const uint4 *A = As + a_off;
         const uint32_t *B = Bs + b_off;
@@ -483,12 +510,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
 
 }  // namespace
 
-hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
-                       const float *gamma, int N, int K, float *Y, int32_t *acc,
-                       hipStream_t s) {
+namespace {
+template <bool A4>
+hipError_t launch_gemm_t(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
+                         const float *gamma, int N, int K, float *Y, int32_t *acc,
+                         hipStream_t s) {
     if (M == 0 || N == 0)
         return hipSuccess;
-    if (M < 128 && gemm_skinny_fits(M, K))
+    if (!A4 && M < 128 && gemm_skinny_fits(M, K))
         return launch_gemm_skinny(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
     if (M >= 128) {
         int cfg = (N >= 4096 && M >= 256) ? 0 : 1;
@@ -497,18 +526,34 @@ hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *W
 #endif
         if (cfg == 0) {
             const int m_tiles = (M + 255) / 256, n_tiles = (N + 255) / 256;
-            hipLaunchKernelGGL((gemm256_kernel<2, 4, 4, 2, false>), dim3(m_tiles * n_tiles), dim3(512), 0,
+            hipLaunchKernelGGL((gemm256_kernel<2, 4, 4, 2, false, A4>), dim3(m_tiles * n_tiles), dim3(512), 0,
                                s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles, GateUp{});
         } else {
             const int m_tiles = (M + 127) / 128, n_tiles = (N + 255) / 256;
-            hipLaunchKernelGGL((gemm256_kernel<2, 4, 2, 2, false>), dim3(m_tiles * n_tiles), dim3(512), 0,
+            hipLaunchKernelGGL((gemm256_kernel<2, 4, 2, 2, false, A4>), dim3(m_tiles * n_tiles), dim3(512), 0,
                                s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles, GateUp{});
         }
         return hipGetLastError();
     }
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-    hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, Xq, d, M, Wp, gamma, N, K, Y, acc);
+    hipLaunchKernelGGL(gemm_kernel<A4>, grid, dim3(256), 0, s, Xq, d, M, Wp, gamma, N, K, Y, acc);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
+                       const float *gamma, int N, int K, float *Y, int32_t *acc,
+                       hipStream_t s) {
+    return launch_gemm_t<false>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+}
+
+hipError_t launch_bitlinear_a4(const uint8_t *Xq4, const float *d, int M, const uint8_t *Wp,
+                               const float *gamma, int N, int K, float *Y, int32_t *acc,
+                               hipStream_t s) {
+    if (M <= kGemvMaxTokens)
+        return launch_gemv_a4(Xq4, d, M, Wp, gamma, N, K, Y, acc, s);
+    return launch_gemm_t<true>(reinterpret_cast<const int8_t *>(Xq4), d, M, Wp, gamma, N, K, Y, acc, s);
 }
 
 hipError_t launch_ffn_gate_up(const int8_t *Xq, const float *d, int M, int K, const uint8_t *Wg,

@@ -67,7 +67,10 @@ __device__ __forceinline__ void load_units(uint4 (&w)[kUnitsInFlight], const uin
         w[j] = ld_stream(wrow + min(u + j * L, ue - 1));   // clamped: always in bounds
 }
 
-template <int L, int MT>
+// A4: the activations are 4-bit codes, two per byte ([M][K/2]); only the
+// staging differs (eight bytes of codes per 16-element group, sign-extended
+// into the same transposed int8 group).
+template <int L, int MT, bool A4 = false>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K, int KC,
@@ -107,8 +110,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         for (int i = tid; i < mt * groups; i += kThreads) {
             const int m = i / groups;
             const int g = i - m * groups;
-            const uint4 v = *reinterpret_cast<const uint4 *>(Xq + (size_t)(m0 + m) * K + kc0 + 16 * g);
-            xs[m * gpc + g] = transpose16(v);
+            if constexpr (A4) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(
+                    Xq + ((size_t)(m0 + m) * K + kc0 + 16 * g) / 2);
+                xs[m * gpc + g] = a4_to_t16(v);
+            } else {
+                const uint4 v = *reinterpret_cast<const uint4 *>(Xq + (size_t)(m0 + m) * K + kc0 + 16 * g);
+                xs[m * gpc + g] = transpose16(v);
+            }
         }
         __syncthreads();
         for (int u = ub + s; u < ue; u += L * kUnitsInFlight) {
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
 }
 
-template <int L, int MT>
+template <int L, int MT, bool A4 = false>
 hipError_t launch_lm(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                      const float *gamma, int N, int K, float *Y, int32_t *acc, hipStream_t s) {
     constexpr int rows_per_wg = (kThreads / 64) * (64 / L);
@@ -154,12 +163,12 @@ hipError_t launch_lm(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
     if (KC > K) KC = K;
     const dim3 grid((N + rows_per_wg - 1) / rows_per_wg, (M + MT - 1) / MT);
     const size_t lds = (size_t)MT * KC;
-    hipLaunchKernelGGL((gemv_kernel<L, MT>), grid, dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((gemv_kernel<L, MT, A4>), grid, dim3(kThreads), lds, s,
                        Xq, d, M, Wp, gamma, N, K, KC, Y, acc);
     return hipGetLastError();
 }
 
-template <int MT>
+template <int MT, bool A4 = false>
 hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                     const float *gamma, int N, int K, float *Y, int32_t *acc, hipStream_t s) {
     const int U = K / 64;                               // 16-byte units per row
@@ -168,10 +177,10 @@ hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
     L = BL_GEMV_FORCE_L;                                // tuning builds only
 #endif
     switch (L) {
-    case 8: return launch_lm<8, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
-    case 16: return launch_lm<16, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
-    case 32: return launch_lm<32, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
-    default: return launch_lm<64, MT>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    case 8: return launch_lm<8, MT, A4>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    case 16: return launch_lm<16, MT, A4>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    case 32: return launch_lm<32, MT, A4>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    default: return launch_lm<64, MT, A4>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
     }
 }
 
@@ -522,6 +531,19 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
 }
 
 }  // namespace
+
+// 4-bit activation codes, 1 <= M <= 8, on the v_dot4 kernel.
+hipError_t launch_gemv_a4(const uint8_t *Xq4, const float *d, int M, const uint8_t *Wp,
+                          const float *gamma, int N, int K, float *Y, int32_t *acc,
+                          hipStream_t s) {
+    if (M == 0 || N == 0)
+        return hipSuccess;
+    const int8_t *X = reinterpret_cast<const int8_t *>(Xq4);
+    if (M == 1) return launch_m<1, true>(X, d, M, Wp, gamma, N, K, Y, acc, s);
+    if (M == 2) return launch_m<2, true>(X, d, M, Wp, gamma, N, K, Y, acc, s);
+    if (M <= 4) return launch_m<4, true>(X, d, M, Wp, gamma, N, K, Y, acc, s);
+    return launch_m<8, true>(X, d, M, Wp, gamma, N, K, Y, acc, s);
+}
 
 hipError_t launch_gemv(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                        const float *gamma, int N, int K, float *Y, int32_t *acc,

@@ -25,12 +25,26 @@ hipError_t noalloc_quant_scratch(double **out);
 // Per-token absmax int8 quantisation; dtype 0 = fp32, 1 = bf16.
 hipError_t launch_quant_act(const void *X, int dtype, int64_t M, int64_t K,
                             int8_t *Xq, float *d, hipStream_t s);
+// Per-token absmax to 4-bit codes, two per byte [M][K/2]; K even.
+hipError_t launch_quant_act4(const void *X, int dtype, int64_t M, int64_t K,
+                             uint8_t *Xq4, float *d, hipStream_t s);
+// Y = float(acc) * fl(gamma * d[m]) with the activations given as 4-bit codes
+// [M][K/2] (any M, K % 64 == 0): the product kernels with their activation
+// staging reading nibbles.
+hipError_t launch_bitlinear_a4(const uint8_t *Xq4, const float *d, int M, const uint8_t *Wp,
+                               const float *gamma, int N, int K, float *Y, int32_t *acc,
+                               hipStream_t s);
 
 // Y = float(acc) * fl(gamma * d[m]), acc = Xq . unpack(Wp)^T.  VALU kernel
 // (v_dot4) for a handful of tokens.
 hipError_t launch_gemv(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
                        const float *gamma, int N, int K, float *Y, int32_t *acc,
                        hipStream_t s);
+
+// The same for 4-bit activation codes ([M][K/2]), 1 <= M <= 8.
+hipError_t launch_gemv_a4(const uint8_t *Xq4, const float *d, int M, const uint8_t *Wp,
+                          const float *gamma, int N, int K, float *Y, int32_t *acc,
+                          hipStream_t s);
 
 // Same product on int8 MFMA tiles, any M.
 hipError_t launch_gemm(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,

@@ -282,7 +282,64 @@ __global__ __launch_bounds__(kActThreads) void quant_act_kernel(const void *__re
         d[m] = act_scale(a);
 }
 
+// 4-bit per-token absmax (BitNet a4.8): one workgroup per token row; the
+// same two passes as quant_act_kernel with act4_code, two codes per byte
+// (element 2b in bits 0..3 of byte b).  K % 8 == 0 takes 8 elements per
+// thread and stores a dword of 8 codes; otherwise pairs and byte stores.
+template <int DT>
+__global__ __launch_bounds__(kActThreads) void quant_act4_kernel(const void *__restrict__ X,
+                                                                 int64_t K,
+                                                                 uint8_t *__restrict__ Xq4,
+                                                                 float *__restrict__ d) {
+    __shared__ float red[kActThreads / 64];
+    const int64_t m = blockIdx.x;
+    const int64_t base = m * K;
+    const bool vec = (K % 8) == 0;
+    float a = 0.0f;
+    if (vec) {
+        for (int64_t k = 8 * (int64_t)threadIdx.x; k < K; k += 8 * kActThreads) {
+            const float4 v0 = load_x4<DT>(X, base + k), v1 = load_x4<DT>(X, base + k + 4);
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+        }
+    } else {
+        for (int64_t k = threadIdx.x; k < K; k += kActThreads)
+            a = fmaxf(a, fabsf(load_x<DT>(X, base + k)));
+    }
+    a = block_max(a, red);
+    const float s = act4_inv_scale(a);
+    uint8_t *row = Xq4 + m * (K / 2);
+    if (vec) {
+        for (int64_t k = 8 * (int64_t)threadIdx.x; k < K; k += 8 * kActThreads) {
+            const float4 v0 = load_x4<DT>(X, base + k), v1 = load_x4<DT>(X, base + k + 4);
+            const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w |= (uint32_t)(act4_code(x[e], s) & 15) << (4 * e);
+            *reinterpret_cast<uint32_t *>(row + k / 2) = w;
+        }
+    } else {
+        for (int64_t b = threadIdx.x; b < K / 2; b += kActThreads) {
+            const int q0 = act4_code(load_x<DT>(X, base + 2 * b), s);
+            const int q1 = act4_code(load_x<DT>(X, base + 2 * b + 1), s);
+            row[b] = (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
+        }
+    }
+    if (threadIdx.x == 0)
+        d[m] = act4_scale(a);
+}
+
 }  // namespace
+
+hipError_t launch_quant_act4(const void *X, int dtype, int64_t M, int64_t K, uint8_t *Xq4, float *d,
+                             hipStream_t s) {
+    if (M == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)M), block(kActThreads);
+    if (dtype == 0) hipLaunchKernelGGL(quant_act4_kernel<0>, grid, block, 0, s, X, K, Xq4, d);
+    else            hipLaunchKernelGGL(quant_act4_kernel<1>, grid, block, 0, s, X, K, Xq4, d);
+    return hipGetLastError();
+}
 
 int64_t quant_weight_blocks(int64_t N, int64_t K) { return (N * K + kBlockTerms - 1) / kBlockTerms; }
 

@@ -94,6 +94,26 @@ def test_product_validation(lib):
     assert lib.bitlinear_gemv(A16, A4, 65, A16, A4, 8, 64, A4, None, None) == SHAPE
 
 
+def test_a4_validation(lib):
+    q4, a4 = lib.quant_act_absmax_i4, lib.bitlinear_a4
+    assert q4(A16, 0, -1, 64, A16, A4, None) == SHAPE
+    assert q4(A16, 0, 2, 65, A16, A4, None) == SHAPE                     # K odd
+    assert q4(A16, 0, 2, 2 * bl.BL_MAX_K, A16, A4, None) == SHAPE
+    assert q4(A16, 9, 2, 64, A16, A4, None) == DTYPE
+    assert q4(None, 0, 0, 64, None, None, None) == OK                    # no rows
+    assert q4(None, 0, 2, 64, A16, A4, None) == NULL
+    assert q4(A16, 0, 2, 64, None, A4, None) == NULL
+    assert q4(A16, 0, 2, 64, A16, None, None) == NULL
+    assert q4(A4, 0, 2, 64, A16, A4, None) == ALIGN
+    assert q4(A16, 0, 2, 64, A4, A4, None) == ALIGN
+    assert q4(A16, 0, 2, 64, A16, A1, None) == ALIGN
+    assert a4(A16, A4, -1, A16, A4, 8, 64, A4, None, None) == SHAPE
+    assert a4(A16, A4, 1, A16, A4, 8, 96, A4, None, None) == SHAPE         # K % 64
+    assert a4(None, None, 0, None, None, 8, 64, None, None, None) == OK
+    assert a4(None, A4, 1, A16, A4, 8, 64, A4, None, None) == NULL
+    assert a4(A4, A4, 1, A16, A4, 8, 64, A4, None, None) == ALIGN
+
+
 def test_noalloc_quant_validation(lib):
     """The allocation-free quantiser's host checks: its scratch holds the
     block sums of at most 2^27 weights."""
