@@ -35,7 +35,8 @@
 // phase's weight loads would wait for all of them; with the roles split, the
 // compute waves issue the next phase's weight loads (and gammas) as soon as
 // their dot products are done, and those stream from HBM while the receivers
-// wait for the next input.
+// wait for the next input; once they have arrived the compute waves unpack
+// up to four units each to int8 values, still before the input is there.
 //
 // Every wait is bounded by a real-time limit (the caller's, 1 s by default).
 // A workgroup that runs out of time (only possible if the grid is not all
@@ -56,6 +57,7 @@ constexpr int kR = 64 * kRecvWaves;           // receiver threads
 constexpr int kC = 512;                       // compute threads
 constexpr int kT = kR + kC;                   // threads per workgroup
 constexpr int kS = 6;                         // packed 16-byte weight units per compute thread
+constexpr int kPU = 4;                        // of them unpacked while the phase input is awaited
 constexpr int kMaxH = 3072;                   // longest H (P0, P1, P2 inputs)
 constexpr int kMaxF = 7168;                   // longest F (P3 input)
 constexpr int kNH = kMaxH / 2 / kR;           // 2-element chunks per receiver, length H
@@ -167,6 +169,7 @@ __device__ __forceinline__ const uint4 *row_ptr(const PArgs &a, const PLayer &L,
 // weight units and the phase's gammas.
 struct Pre {
     uint4 w[kS];
+    uint4 v[kPU][4];                          // units i < kPU unpacked: v[i][t] from dword t
     float g0, g1, g2;
 };
 
@@ -197,6 +200,25 @@ __device__ __forceinline__ void prefetch(const PArgs &a, const PLayer &L, int ct
     if (P == 1) pre.g0 = scalar_load(L.g[3]);
     if (P == 2) { pre.g0 = scalar_load(L.g[4]); pre.g1 = scalar_load(L.g[5]); }
     if (P == 3) pre.g0 = scalar_load(L.g[6]);
+}
+
+// Unpacks the first kPU loaded units of phase P (the first matrix of a
+// pair) into int8 values, so that after the input arrives only the v_dot4
+// work remains for them.  Run between the loads and the wait for the input.
+template <int P>
+__device__ __forceinline__ void unpack_pre(const PArgs &a, Pre &pre) {
+    const int ns = a.nslot[P];
+    constexpr int half = P == 2 ? kS / 2 : kS;
+    constexpr int nu = half < kPU ? half : kPU;
+#pragma unroll
+    for (int i = 0; i < nu; ++i) {
+        if (i < ns) {
+            const uint32_t dw[4] = {pre.w[i].x, pre.w[i].y, pre.w[i].z, pre.w[i].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                unpack16(dw[t], pre.v[i][t].x, pre.v[i][t].y, pre.v[i][t].z, pre.v[i][t].w);
+        }
+    }
 }
 
 struct Smem {
@@ -462,27 +484,27 @@ __device__ __forceinline__ bool quantise(const PArgs &a, Smem &sm, int K, float 
     for (int w = 1; w < kRecvWaves; ++w) am = fmaxf(am, sm.red_a[w]);
     const float sc = act_inv_scale(am);
     const int U = K / 64;
-    for (int g = threadIdx.x; g < K / 16; g += kT) {
-        const float4 *src = reinterpret_cast<const float4 *>(sm.vals + 16 * g);
-        uint32_t q4[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float4 x = src[t];
-            q4[t] = (uint32_t)(act_code(x.x, sc) & 0xFF) |
-                    ((uint32_t)(act_code(x.y, sc) & 0xFF) << 8) |
-                    ((uint32_t)(act_code(x.z, sc) & 0xFF) << 16) |
-                    ((uint32_t)(act_code(x.w, sc) & 0xFF) << 24);
-        }
-        sm.xs[(g & 3) * U + (g >> 2)] = transpose16(make_uint4(q4[0], q4[1], q4[2], q4[3]));
+    // One code dword per thread and step (all waves take part): dword t of
+    // group g holds elements 16 g + t + 4 j in byte j, the transposed order.
+    uint32_t *xd = reinterpret_cast<uint32_t *>(sm.xs);
+    for (int q = threadIdx.x; q < K / 4; q += kT) {
+        const int g = q >> 2, t = q & 3;
+        const float *src = sm.vals + 16 * g + t;
+        xd[((g & 3) * U + (g >> 2)) * 4 + t] =
+            (uint32_t)(act_code(src[0], sc) & 0xFF) |
+            ((uint32_t)(act_code(src[4], sc) & 0xFF) << 8) |
+            ((uint32_t)(act_code(src[8], sc) & 0xFF) << 16) |
+            ((uint32_t)(act_code(src[12], sc) & 0xFF) << 24);
     }
     __syncthreads();
     return true;
 }
 
 // one 16-byte weight unit (64 weights) against activation groups 4u..4u+3,
-// into four independent accumulators
-__device__ __forceinline__ void dot_unit(const uint4 &w, const uint4 *xs, int U, int u,
-                                         int (&acc)[4]) {
+// into four independent accumulators: from the packed unit, or (dot_unit)
+// from its values unpacked ahead
+__device__ __forceinline__ void dot_unit_packed(const uint4 &w, const uint4 *xs, int U, int u,
+                                                int (&acc)[4]) {
     const uint32_t dws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -493,6 +515,17 @@ __device__ __forceinline__ void dot_unit(const uint4 &w, const uint4 *xs, int U,
         acc[1] = dot4(v1, xv.y, acc[1]);
         acc[2] = dot4(v2, xv.z, acc[2]);
         acc[3] = dot4(v3, xv.w, acc[3]);
+    }
+}
+__device__ __forceinline__ void dot_unit(const uint4 (&v)[4], const uint4 *xs, int U, int u,
+                                         int (&acc)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint4 xv = xs[t * U + u];
+        acc[0] = dot4(v[t].x, xv.x, acc[0]);
+        acc[1] = dot4(v[t].y, xv.y, acc[1]);
+        acc[2] = dot4(v[t].z, xv.z, acc[2]);
+        acc[3] = dot4(v[t].w, xv.w, acc[3]);
     }
 }
 
@@ -513,8 +546,9 @@ __device__ __forceinline__ bool dot_phase(const PArgs &a, const Smem &sm, const 
         for (int i = 0; i < half; ++i) {
             const int u = s + (i << ls);
             if (i < ns && u < U) {
-                dot_unit(pre.w[i], sm.xs, U, u, c0);
-                if (P == 2) dot_unit(pre.w[half + i], sm.xs, U, u, c1);
+                if (i < kPU) dot_unit(pre.v[i < kPU ? i : 0], sm.xs, U, u, c0);
+                else dot_unit_packed(pre.w[i], sm.xs, U, u, c0);
+                if (P == 2) dot_unit_packed(pre.w[half + i], sm.xs, U, u, c1);
             }
         }
     }
@@ -578,6 +612,7 @@ __device__ __forceinline__ void compute_loop(const PArgs &a, Smem &sm) {
         float am;
 
         // P0: q, k, v
+        unpack_pre<0>(a, pre);
         if (!quantise(a, sm, H, am)) return;
         float d = act_scale(am);
         wg_rows(H + 2 * KV, r0, nr);
@@ -600,6 +635,7 @@ __device__ __forceinline__ void compute_loop(const PArgs &a, Smem &sm) {
         prefetch<1>(a, L, ct, pre);
 
         // P1: o
+        unpack_pre<1>(a, pre);
         if (!quantise(a, sm, H, am)) return;
         d = act_scale(am);
         wg_rows(H, r0, nr);
@@ -612,6 +648,7 @@ __device__ __forceinline__ void compute_loop(const PArgs &a, Smem &sm) {
         prefetch<2>(a, L, ct, pre);
 
         // P2: gate/up pairs -> H
+        unpack_pre<2>(a, pre);
         if (!quantise(a, sm, H, am)) return;
         d = act_scale(am);
         wg_rows(F, r0, nr);
@@ -625,6 +662,7 @@ __device__ __forceinline__ void compute_loop(const PArgs &a, Smem &sm) {
         prefetch<3>(a, L, ct, pre);
 
         // P3: down -> y, with dz = (max|Z| / 127) / rms(H)
+        unpack_pre<3>(a, pre);
         if (!quantise(a, sm, F, am)) return;
         double ss = sm.red_s[0];
 #pragma unroll
