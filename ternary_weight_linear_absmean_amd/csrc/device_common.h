@@ -82,6 +82,41 @@ __device__ __forceinline__ uint4 a4_to_t16(uint2 p) {
     return t;
 }
 
+// Reductions across lanes.  Steps inside a row of 16 lanes go through DPP
+// (no LDS round trip, unlike a ds_bpermute shuffle): xor 1 and xor 2 as quad
+// permutes, then the mirrored lane of the 8-lane half-row and of the row.
+// After the steps for a group of G lanes (G a power of two, groups aligned
+// to G) every lane of the group holds the group's sum (or maximum); groups
+// of 32 and 64 lanes add shuffle steps.  The combination order differs from
+// a plain butterfly, so these serve order-free reductions only (integer
+// sums, maxima).  Call them with every lane of the wave active.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int group_sum(int v, int G) {
+    if (G >= 2) v += dpp_i32<kDppXor1>(v);
+    if (G >= 4) v += dpp_i32<kDppXor2>(v);
+    if (G >= 8) v += dpp_i32<kDppHalfMirror>(v);
+    if (G >= 16) v += dpp_i32<kDppMirror>(v);
+    if (G >= 32) v += __shfl_xor(v, 16);
+    if (G >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+__device__ __forceinline__ float group_max(float v, int G) {
+    if (G >= 2) v = fmaxf(v, __int_as_float(dpp_i32<kDppXor1>(__float_as_int(v))));
+    if (G >= 4) v = fmaxf(v, __int_as_float(dpp_i32<kDppXor2>(__float_as_int(v))));
+    if (G >= 8) v = fmaxf(v, __int_as_float(dpp_i32<kDppHalfMirror>(__float_as_int(v))));
+    if (G >= 16) v = fmaxf(v, __int_as_float(dpp_i32<kDppMirror>(__float_as_int(v))));
+    if (G >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    if (G >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }

@@ -138,11 +138,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
 
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-        for (int off = L / 2; off > 0; off >>= 1)
-            acc[m] += __shfl_xor(acc[m], off);
-    }
+    for (int m = 0; m < MT; ++m) acc[m] = group_sum(acc[m], L);
     if (row < N && s == 0) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -360,9 +356,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1)
-                amax[m] = fmaxf(amax[m], __shfl_xor(amax[m], off));
+            amax[m] = group_max(amax[m], 64);
         }
         if (lane == 0) {
 #pragma unroll
@@ -477,7 +471,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         const int c = L >> 2;
         const int jc = lane % c;
         int v = jc == 0 ? acc4[0] : jc == 1 ? acc4[1] : jc == 2 ? acc4[2] : acc4[3];
-        for (int off = c >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        v = group_sum(v, c);
         if (lane < 16 && jc == 0 && row < N) {
             float a = red[0][0];
 #pragma unroll
@@ -510,9 +504,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         }
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-        for (int off = L >> 1; off > 0; off >>= 1)
-            acc[m] += __shfl_xor(acc[m], off);
+    for (int m = 0; m < MT; ++m) acc[m] = group_sum(acc[m], L);
     if (row < N && s == 0) {
         const float g = gam;
         float dm[MT];

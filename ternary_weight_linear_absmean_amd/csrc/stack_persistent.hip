@@ -327,11 +327,7 @@ __device__ __forceinline__ void keep(uint2 *dst, int n, int c, float2 x, unsigne
     if (tr) *reinterpret_cast<float2 *>(tr + 2 * c) = x;
 }
 
-__device__ __forceinline__ float wave_max(float a) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-    return a;
-}
+__device__ __forceinline__ float wave_max(float a) { return group_max(a, 64); }
 
 // P0 input: x of global layer lg (x_in for the call's first layer, else
 // x_mid + y of the layer before); workgroup 0 keeps it as xa.
@@ -558,10 +554,8 @@ __device__ __forceinline__ bool dot_phase(const PArgs &a, const Smem &sm, const 
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
     acc0 = (c0[0] + c0[1]) + (c0[2] + c0[3]);
     acc1 = (c1[0] + c1[1]) + (c1[2] + c1[3]);
-    for (int off = (1 << ls) >> 1; off > 0; off >>= 1) {
-        acc0 += __shfl_xor(acc0, off);
-        if (P == 2) acc1 += __shfl_xor(acc1, off);
-    }
+    acc0 = group_sum(acc0, 1 << ls);
+    if (P == 2) acc1 = group_sum(acc1, 1 << ls);
     return rg < nr && s == 0;
 }
 

@@ -193,9 +193,7 @@ __global__ __launch_bounds__(kT5Threads) void gemv_t5_kernel(
         }
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int off = L / 2; off > 0; off >>= 1) acc[m] += __shfl_xor(acc[m], off);
+    for (int m = 0; m < MT; ++m) acc[m] = group_sum(acc[m], L);
     if (row < N && s == 0) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
