@@ -131,7 +131,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 // sustains about twice the throughput of 16x16x64 in a plain MFMA loop).
 // Workgroup = WM x WN waves, each wave owns MI x NJ blocks of 32 x 32 of Y
 // (16 MI NJ int32 accumulators per lane); tile = 32 MI WM x 32 NJ WN.
-//   <2, 4, 4, 2>: 256 x 256 tiles, 512 threads (wide N, e.g. K2560 -> N6912)
+//   <1, 4, 4, 2>: 128 x 256 tiles, 256 threads, two workgroups per CU (wide
+//                 N, e.g. K2560 -> N6912): each SIMD runs one wave of each
+//                 workgroup, and the two workgroups meet at their own
+//                 barriers, so a SIMD's two waves are not held in step;
+//                 44.0-44.8 us at M = 2048 against 45.5-46.1 us for
+//                 256 x 256 tiles of 8 waves (<2, 4, 4, 2>) with the same loop
 //   <2, 4, 2, 2>: 128 x 256 tiles, 512 threads (narrow N, e.g. K6912 -> N2560,
 //                 where 256 x 256 tiles would leave most CUs idle): measured
 //                 59 us on M2048 K6912 N2560 against 73 us for 128 x 128
@@ -308,7 +313,7 @@ __device__ __forceinline__ void gate_up_epilogue(const v16i (&acc)[MI2][2], floa
 }
 
 template <int WM, int WN, int MI2, int NJ2, bool GU, bool A4 = false>
-__global__ __launch_bounds__(64 * WM * WN) void gemm256_kernel(
+__global__ __launch_bounds__(64 * WM * WN, WM * WN == 4 ? 2 : 1) void gemm256_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
     float *__restrict__ Y, int32_t *__restrict__ acc_out, int m_tiles, const GateUp gu) {
@@ -525,8 +530,8 @@ hipError_t launch_gemm_t(const int8_t *Xq, const float *d, int M, const uint8_t 
         cfg = BL_GEMM_CFG;                        // tuning builds only
 #endif
         if (cfg == 0) {
-            const int m_tiles = (M + 255) / 256, n_tiles = (N + 255) / 256;
-            hipLaunchKernelGGL((gemm256_kernel<2, 4, 4, 2, false, A4>), dim3(m_tiles * n_tiles), dim3(512), 0,
+            const int m_tiles = (M + 127) / 128, n_tiles = (N + 255) / 256;
+            hipLaunchKernelGGL((gemm256_kernel<1, 4, 4, 2, false, A4>), dim3(m_tiles * n_tiles), dim3(256), 0,
                                s, Xq, d, M, Wp, gamma, N, K, Y, acc, m_tiles, GateUp{});
         } else {
             const int m_tiles = (M + 127) / 128, n_tiles = (N + 255) / 256;
