@@ -186,13 +186,15 @@ hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
 // dealt to jobs in order (job j owns workgroups [wg_begin_j, wg_begin_j+1)).
 // A workgroup's waves have two roles:
 //   quantising waves (4) read the job's activation rows (L2-resident after
-//     the first workgroup), form max |x| per token and write the int8 codes
-//     into LDS in transposed 16-byte groups (the job's first workgroup also
-//     stores Xq and d to memory); they publish each step by counting up an
-//     LDS word;
+//     the first workgroup) into LDS and form max |x| per token, publishing
+//     it by counting up an LDS word;
 //   compute waves (8) issue all their packed-weight loads at once, wait for
-//     the codes count, then run the unit loop and lane reduction of
-//     gemv_kernel, with the lane split L chosen per job.
+//     that count;
+//   then all twelve waves write the int8 codes into LDS in transposed 16-byte
+//     groups (the job's first workgroup also stores Xq and d to memory) and
+//     count up a second word, and the compute waves, once it reaches twelve,
+//     run the unit loop and lane reduction of gemv_kernel, with the lane
+//     split L chosen per job.
 // The roles are split because a wave cannot issue past a load instruction
 // the memory pipeline has not accepted: with the weight requests of the whole
 // launch in flight, a wave that issued weight loads reaches the next
@@ -300,10 +302,47 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     }
     __syncthreads();                            // nothing is in flight yet
 
+    const int gsz = dtype == 0 ? 4 : 2;                           // uint4 per 16 elements
+    uint4 *xraw = xs + MT * gpc;                                   // [MT][K / 16][gsz]
+    const bool writer = (wg == 0);
+    // The int8 codes of groups g = first, first + kFThreads, ... from the raw
+    // rows in LDS, once every quantising wave's maximum is in red[][]: all
+    // twelve waves take part, the compute waves while their weights stream.
+    auto form_codes = [&](int first) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float a = red[0][m];
+#pragma unroll
+            for (int v = 1; v < kQWaves; ++v) a = fmaxf(a, red[v][m]);
+            if (m < mt) {
+                const float sc = act_inv_scale(a);
+                for (int g = first; g < gpc; g += kFThreads) {
+                    uint4 raw[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (t < gsz) raw[t] = xraw[((size_t)m * gpc + g) * gsz + t];
+                    float x[16];
+                    unpack_x16(raw, dtype, x);
+                    uint32_t q4[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        q4[t] = (uint32_t)(act_code(x[4 * t], sc) & 0xFF) |
+                                ((uint32_t)(act_code(x[4 * t + 1], sc) & 0xFF) << 8) |
+                                ((uint32_t)(act_code(x[4 * t + 2], sc) & 0xFF) << 16) |
+                                ((uint32_t)(act_code(x[4 * t + 3], sc) & 0xFF) << 24);
+                    const uint4 qv = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+                    if (writer && jb.Xq)
+                        *reinterpret_cast<uint4 *>(jb.Xq + (size_t)(m0 + m) * K + 16 * g) = qv;
+                    xs[m * gpc + g] = transpose16(qv);
+                }
+                if (writer && jb.d && first == 0)
+                    jb.d[m0 + m] = act_scale(a);
+            }
+        }
+    };
+
     if (tid < kQThreads) {
-        // ---- quantising waves: the job's activation rows -> int8 codes in LDS
-        const int gsz = dtype == 0 ? 4 : 2;                       // uint4 per 16 elements
-        uint4 *xraw = xs + MT * gpc;                               // [MT][K / 16][gsz]
+        // ---- quantising waves: the job's activation rows -> max |x| in LDS
         const char *xbase = reinterpret_cast<const char *>(jb.X);
         const int ng = mt * gpc;                                   // (token, group) pairs
         uint4 xr[kXPre][4];
@@ -367,37 +406,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
             __hip_atomic_fetch_add(&n_amax, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         while (__hip_atomic_load(&n_amax, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kQWaves)
             __builtin_amdgcn_s_sleep(1);
-        const bool writer = (wg == 0);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            float a = red[0][m];
-#pragma unroll
-            for (int v = 1; v < kQWaves; ++v) a = fmaxf(a, red[v][m]);
-            if (m < mt) {
-                const float sc = act_inv_scale(a);
-                for (int g = tid; g < gpc; g += kQThreads) {
-                    uint4 raw[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        if (t < gsz) raw[t] = xraw[((size_t)m * gpc + g) * gsz + t];
-                    float x[16];
-                    unpack_x16(raw, dtype, x);
-                    uint32_t q4[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        q4[t] = (uint32_t)(act_code(x[4 * t], sc) & 0xFF) |
-                                ((uint32_t)(act_code(x[4 * t + 1], sc) & 0xFF) << 8) |
-                                ((uint32_t)(act_code(x[4 * t + 2], sc) & 0xFF) << 16) |
-                                ((uint32_t)(act_code(x[4 * t + 3], sc) & 0xFF) << 24);
-                    const uint4 qv = make_uint4(q4[0], q4[1], q4[2], q4[3]);
-                    if (writer && jb.Xq)
-                        *reinterpret_cast<uint4 *>(jb.Xq + (size_t)(m0 + m) * K + 16 * g) = qv;
-                    xs[m * gpc + g] = transpose16(qv);
-                }
-                if (writer && jb.d && tid == 0)
-                    jb.d[m0 + m] = act_scale(a);
-            }
-        }
+        form_codes(tid);
         // the codes in LDS before the count the compute waves wait for
         if (lane == 0)
             __hip_atomic_fetch_add(&n_codes, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -424,8 +433,15 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
 #pragma unroll
     for (int q = 0; q < kFUnits; ++q)
         w[q] = ld_stream(wrow + min(sig + q * L, U - 1));  // a job with N == 0 reads its own X here
+    // the maxima, then this wave's share of the codes, then everyone's
+    while (__hip_atomic_load(&n_amax, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kQWaves)
+        __builtin_amdgcn_s_sleep(1);
+    form_codes(kQThreads + ct);
+    if (lane == 0)
+        __hip_atomic_fetch_add(&n_codes, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    while (__hip_atomic_load(&n_codes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kQWaves)
+    while (__hip_atomic_load(&n_codes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
+           (unsigned)(kFThreads / 64))
         __builtin_amdgcn_s_sleep(1);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
