@@ -17,6 +17,8 @@
 // order that the unpacked weights come out in.  The int32 partial sums of a
 // row are added across its L lanes with cross-lane shuffles, and the lane
 // that ends with the row's sum applies the fp32 rescale.
+#include <climits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -186,15 +188,14 @@ hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
 // dealt to jobs in order (job j owns workgroups [wg_begin_j, wg_begin_j+1)).
 // A workgroup's waves have two roles:
 //   quantising waves (4) read the job's activation rows (L2-resident after
-//     the first workgroup) into LDS and form max |x| per token, publishing
-//     it by counting up an LDS word;
-//   compute waves (8) issue all their packed-weight loads at once, wait for
-//     that count;
-//   then all twelve waves write the int8 codes into LDS in transposed 16-byte
+//     the first workgroup) into LDS, form max |x| per token (counting up an
+//     LDS word), then write the int8 codes into LDS in transposed 16-byte
 //     groups (the job's first workgroup also stores Xq and d to memory) and
-//     count up a second word, and the compute waves, once it reaches twelve,
-//     run the unit loop and lane reduction of gemv_kernel, with the lane
-//     split L chosen per job.
+//     count up a second word;
+//   compute waves (8) issue all their packed-weight loads at once, unpack
+//     the first units as they land while the codes are being formed, and once
+//     the second count reaches four run the unit loop and lane reduction of
+//     gemv_kernel, with the lane split L chosen per job.
 // The roles are split because a wave cannot issue past a load instruction
 // the memory pipeline has not accepted: with the weight requests of the whole
 // launch in flight, a wave that issued weight loads reaches the next
@@ -203,7 +204,16 @@ hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
 // to about when the weights had landed (codes 3.1 us after the workgroup
 // start, 2.9 us of which waiting); with the quantising waves issuing no
 // weight loads and no barrier, the four decode shapes' step went from 7.2 to
-// 6.35 us.
+// 6.35 us.  For the same reason the compute waves form no codes: some of them
+// are still held at their weight-load issue when max |x| is known, and codes
+// that waited for all twelve waves came about 1 us after the quantising
+// waves' own.
+// The arguments sit in the kernarg segment, which the waves read with scalar
+// loads whose every wait is a round trip to L2.  The layout keeps the chain
+// before the first weight and activation loads to two such trips: the header
+// (token count and each job's first workgroup, unused jobs at INT_MAX) in one
+// load, then the workgroup's job record (64 bytes) in one load.  Gamma is
+// read on the vector path instead, behind the weights.
 struct FusedJob {
     const void *X;
     const uint8_t *Wp;
@@ -212,13 +222,14 @@ struct FusedJob {
     int8_t *Xq;
     float *d;
     int N, K, dtype, lshift;          // lanes per row L = 1 << lshift
-    int wg_begin, pad;
 };
 
 struct FusedArgs {
+    int M, pad;
+    int wg_begin[kMaxJobs];
     FusedJob job[kMaxJobs];
-    int count, M;
 };
+static_assert(sizeof(FusedJob) == 64, "one 64-byte scalar load per job record");
 
 // 512 compute threads: every workgroup quantises its job's whole activation
 // row, so fewer, larger workgroups repeat that less; on the four 2B-class
@@ -232,6 +243,11 @@ constexpr int kFThreads = kQThreads + kCThreads;
 // splits below a lane owns at most 108 / 16 < 8 units of a row.
 constexpr int kFUnits = 8;
 constexpr int kXPre = 2;            // activation groups per thread loaded ahead of the weights
+// Weight units a compute wave unpacks while the codes are being formed (as
+// far as they have landed): two measured 5.81-5.83 us per step on the four
+// decode shapes, three 5.84-5.86, four 5.88, none 5.95-5.97; the unpacked
+// units stay in registers (16 each) until the codes are there.
+constexpr int kPreUnits = 2;
 
 // Token counts that take the MFMA dot products (the rest use v_dot4).
 #ifndef BL_FUSED_MFMA_MAX_MT
@@ -282,16 +298,18 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     extern __shared__ uint4 xs[];   // [MT][K / 16] transposed code groups, then the raw activations
     __shared__ float red[kQWaves][MT];
     __shared__ unsigned n_amax, n_codes;        // quantising waves past each step
-    int j = 0;
-    for (int t = 1; t < args.count; ++t)
-        if ((int)blockIdx.x >= args.job[t].wg_begin) j = t;
-    const FusedJob &jb = args.job[j];
+    int j = 0, jbegin = 0;
+#pragma unroll
+    for (int t = 1; t < kMaxJobs; ++t)
+        if ((int)blockIdx.x >= args.wg_begin[t]) {
+            j = t;
+            jbegin = args.wg_begin[t];
+        }
+    const FusedJob jb = args.job[j];                // the record, copied by one load
     const int K = jb.K, N = jb.N, dtype = jb.dtype, lshift = jb.lshift;
-    // gamma now, not after the dot products (a job with no rows has none)
-    const float gam = N > 0 ? scalar_load(jb.gamma) : 0.0f;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wg = (int)blockIdx.x - jb.wg_begin;
+    const int wg = (int)blockIdx.x - jbegin;
     const int m0 = blockIdx.y * MT;
     const int mt = min(MT, args.M - m0);
     const int U = K / 64;
@@ -305,9 +323,8 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     const int gsz = dtype == 0 ? 4 : 2;                           // uint4 per 16 elements
     uint4 *xraw = xs + MT * gpc;                                   // [MT][K / 16][gsz]
     const bool writer = (wg == 0);
-    // The int8 codes of groups g = first, first + kFThreads, ... from the raw
-    // rows in LDS, once every quantising wave's maximum is in red[][]: all
-    // twelve waves take part, the compute waves while their weights stream.
+    // The int8 codes of groups g = first, first + kQThreads, ... from the raw
+    // rows in LDS, once every quantising wave's maximum is in red[][].
     auto form_codes = [&](int first) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -316,7 +333,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
             for (int v = 1; v < kQWaves; ++v) a = fmaxf(a, red[v][m]);
             if (m < mt) {
                 const float sc = act_inv_scale(a);
-                for (int g = first; g < gpc; g += kFThreads) {
+                for (int g = first; g < gpc; g += kQThreads) {
                     uint4 raw[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
@@ -433,23 +450,39 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
 #pragma unroll
     for (int q = 0; q < kFUnits; ++q)
         w[q] = ld_stream(wrow + min(sig + q * L, U - 1));  // a job with N == 0 reads its own X here
-    // the maxima, then this wave's share of the codes, then everyone's
-    while (__hip_atomic_load(&n_amax, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kQWaves)
-        __builtin_amdgcn_s_sleep(1);
-    form_codes(kQThreads + ct);
-    if (lane == 0)
-        __hip_atomic_fetch_add(&n_codes, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    while (__hip_atomic_load(&n_codes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
-           (unsigned)(kFThreads / 64))
-        __builtin_amdgcn_s_sleep(1);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // gamma on the vector path, behind the weights (the products need it
+    // only after every weight has landed; a job with no rows has none)
+    const float gam = N > 0 ? __builtin_nontemporal_load(jb.gamma) : 0.0f;
+    auto codes_ready = [&]() {
+        return __hip_atomic_load(&n_codes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >=
+               (unsigned)kQWaves;
+    };
 
     if constexpr (kMfma) {
         // dot products on MFMA over the lane's units; slots past the row's
         // last unit take zero weights (the loop is wave-uniform)
         static_assert(MT == 1, "the MFMA mapping carries one token");
         const int nslot = (U + L - 1) / L;
+        // Until the codes are complete, unpack the first units as they land
+        // (the test between units is wave-uniform: one LDS word).
+        uint4 bpre[kPreUnits][4];
+        int npre = kPreUnits;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+        for (int q = 0; q < kPreUnits; ++q) {
+            if (__builtin_amdgcn_readfirstlane((int)codes_ready())) {
+                npre = q;
+                break;
+            }
+            const bool ok = q < nslot && sig + q * L < U;
+            const uint32_t dws[4] = {ok ? w[q].x : 0u, ok ? w[q].y : 0u, ok ? w[q].z : 0u,
+                                     ok ? w[q].w : 0u};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) unpack16(dws[t], bpre[q][t].x, bpre[q][t].y, bpre[q][t].z, bpre[q][t].w);
+        }
+        while (!codes_ready())
+            __builtin_amdgcn_s_sleep(1);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         v4i acc4 = v4i{0, 0, 0, 0};
         for (int i0 = 0; i0 < nslot; i0 += kFUnits) {
             uint4 wn[kFUnits];
@@ -465,17 +498,22 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
                     const int u = sig + (i0 + q) * L;
                     const bool ok = u < U;
                     const int uc = min(u, U - 1);
-                    // selects rather than a branch on the last slot: branches
-                    // keep the compiler from interleaving consecutive units
-                    const uint32_t dws[4] = {ok ? w[q].x : 0u, ok ? w[q].y : 0u, ok ? w[q].z : 0u,
-                                             ok ? w[q].w : 0u};
+                    uint4 bv[4];
+                    if (q < kPreUnits && i0 == 0 && q < npre) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        uint4 bv;
-                        unpack16(dws[t], bv.x, bv.y, bv.z, bv.w);
-                        acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(xs[4 * uc + t]), as_v4i(bv),
-                                                                     acc4, 0, 0, 0);
+                        for (int t = 0; t < 4; ++t) bv[t] = bpre[q < kPreUnits ? q : 0][t];
+                    } else {
+                        // selects rather than a branch on the last slot: branches
+                        // keep the compiler from interleaving consecutive units
+                        const uint32_t dws[4] = {ok ? w[q].x : 0u, ok ? w[q].y : 0u, ok ? w[q].z : 0u,
+                                                 ok ? w[q].w : 0u};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) unpack16(dws[t], bv[t].x, bv[t].y, bv[t].z, bv[t].w);
                     }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(xs[4 * uc + t]), as_v4i(bv[t]),
+                                                                     acc4, 0, 0, 0);
                 }
             }
             if (more) {
@@ -496,6 +534,10 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         }
         return;
     }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    while (!codes_ready())
+        __builtin_amdgcn_s_sleep(1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
     // dot products over this lane's units, software-pipelined
     int acc[MT];
@@ -584,8 +626,8 @@ hipError_t launch_fused_mt(const FusedArgs &a, int grid_x, int max_k, int max_es
 
 hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t s) {
     FusedArgs a = {};
-    a.count = count;
     a.M = M;
+    for (int j = 0; j < kMaxJobs; ++j) a.wg_begin[j] = INT_MAX;
     int wg = 0, max_k = 0, max_es = 2;
     for (int j = 0; j < count; ++j) {
         FusedJob &f = a.job[j];
@@ -603,7 +645,7 @@ hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t 
         f.lshift = BL_FUSED_LSHIFT;                     // tuning builds only
 #endif
         const int rows_per_wg = (kCThreads / 64) * (64 >> f.lshift);
-        f.wg_begin = wg;
+        a.wg_begin[j] = wg;
         // a job with N == 0 still gets one workgroup when it must write Xq / d
         const int n_wg = f.N > 0 ? (f.N + rows_per_wg - 1) / rows_per_wg : ((f.Xq || f.d) ? 1 : 0);
         // A job with no output rows only quantises; its weight-row pointer
