@@ -358,7 +358,13 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         }
     };
 
-    if (tid < kQThreads) {
+    // The quantising waves' code is laid out first, right after the common
+    // prologue: the instruction cache is cold at each launch, and a far jump
+    // costs a fetch from L2.  The compute waves take that jump instead, which
+    // also puts the activation requests ahead of the weight stream on the
+    // CU (5.55-5.62 against 5.82 us per step with the compute path first;
+    // issuing the weight loads before the role split: 6.56 us).
+    if (__builtin_expect(tid < kQThreads, 1)) {
         // ---- quantising waves: the job's activation rows -> max |x| in LDS
         const char *xbase = reinterpret_cast<const char *>(jb.X);
         const int ng = mt * gpc;                                   // (token, group) pairs
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
 #pragma unroll
         for (int p = 0; p < kXPre; ++p) {
             const int e = min(tid + p * kQThreads, ng - 1);
-            const int m = e / gpc, g = e - m * gpc;
+            const int m = MT == 1 ? 0 : e / gpc, g = e - m * gpc;   // one token: no division
             const uint4 *src = reinterpret_cast<const uint4 *>(xbase + (size_t)(m0 + m) * K * gsz) +
                                (size_t)g * gsz;
             if (dtype == 0) {
@@ -381,7 +387,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
 #pragma unroll
         for (int m = 0; m < MT; ++m) amax[m] = 0.0f;
         auto stage = [&](const uint4 (&raw)[4], int e) {
-            const int m = e / gpc, g = e - m * gpc;
+            const int m = MT == 1 ? 0 : e / gpc, g = e - m * gpc;   // one token: no division
             float x[16];
             unpack_x16(raw, dtype, x);
             uint4 *dst = xraw + ((size_t)m * gpc + g) * gsz;
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
             if (e < ng) stage(xr[p], e);
         }
         for (int e = tid + kXPre * kQThreads; e < ng; e += kQThreads) {
-            const int m = e / gpc, g = e - m * gpc;
+            const int m = MT == 1 ? 0 : e / gpc, g = e - m * gpc;   // one token: no division
             const uint4 *src = reinterpret_cast<const uint4 *>(xbase + (size_t)(m0 + m) * K * gsz) +
                                (size_t)g * gsz;
             uint4 raw[4];
@@ -438,9 +444,10 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     const int rows_wg = (kCThreads / 64) * (64 >> lshift);
     int row, sig;
     if constexpr (kMfma) {
-        const int c = L >> 2, i = lane & 15;                 // columns per row, column
-        row = wg * rows_wg + (ct >> 6) * (64 >> lshift) + i / c;
-        sig = i % c + c * (lane >> 4);
+        // c = L / 4 columns per row (a power of two), column i
+        const int cs = lshift - 2, c = 1 << cs, i = lane & 15;
+        row = wg * rows_wg + (ct >> 6) * (64 >> lshift) + (i >> cs);
+        sig = (i & (c - 1)) + c * (lane >> 4);
     } else {
         row = wg * rows_wg + (ct >> 6) * (64 >> lshift) + r;
         sig = s;
@@ -462,7 +469,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         // dot products on MFMA over the lane's units; slots past the row's
         // last unit take zero weights (the loop is wave-uniform)
         static_assert(MT == 1, "the MFMA mapping carries one token");
-        const int nslot = (U + L - 1) / L;
+        const int nslot = (U + L - 1) >> lshift;
         // Until the codes are complete, unpack the first units as they land
         // (the test between units is wave-uniform: one LDS word).
         uint4 bpre[kPreUnits][4];
@@ -523,8 +530,10 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
         }
         // lane i < 16: D[i % c][i], then the sum over the row's c columns
         const int c = L >> 2;
-        const int jc = lane % c;
-        int v = jc == 0 ? acc4[0] : jc == 1 ? acc4[1] : jc == 2 ? acc4[2] : acc4[3];
+        const int jc = lane & (c - 1);
+        const int v01 = (jc & 1) ? acc4[1] : acc4[0];
+        const int v23 = (jc & 1) ? acc4[3] : acc4[2];
+        int v = (jc & 2) ? v23 : v01;
         v = group_sum(v, c);
         if (lane < 16 && jc == 0 && row < N) {
             float a = red[0][0];
