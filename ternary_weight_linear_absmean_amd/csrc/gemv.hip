@@ -17,6 +17,7 @@
 // order that the unpacked weights come out in.  The int32 partial sums of a
 // row are added across its L lanes with cross-lane shuffles, and the lane
 // that ends with the row's sum applies the fp32 rescale.
+#include <algorithm>
 #include <climits>
 
 #include "device_common.h"
@@ -638,11 +639,18 @@ hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t 
     a.M = M;
     for (int j = 0; j < kMaxJobs; ++j) a.wg_begin[j] = INT_MAX;
     int wg = 0, max_k = 0, max_es = 2;
+    // Jobs in order of decreasing K (stable): the longest workgroups are
+    // dispatched first.  Each job keeps its own outputs, so the order changes
+    // no result.
+    int order[kMaxJobs];
+    for (int j = 0; j < count; ++j) order[j] = j;
+    std::stable_sort(order, order + count, [&](int x, int y) { return jobs[x].K > jobs[y].K; });
     for (int j = 0; j < count; ++j) {
         FusedJob &f = a.job[j];
-        f.X = jobs[j].X; f.Wp = jobs[j].Wp; f.gamma = jobs[j].gamma; f.Y = jobs[j].Y;
-        f.Xq = jobs[j].Xq; f.d = jobs[j].d;
-        f.N = jobs[j].N; f.K = jobs[j].K; f.dtype = jobs[j].dtype;
+        const GemvJob &src = jobs[order[j]];
+        f.X = src.X; f.Wp = src.Wp; f.gamma = src.gamma; f.Y = src.Y;
+        f.Xq = src.Xq; f.d = src.d;
+        f.N = src.N; f.K = src.K; f.dtype = src.dtype;
         // Lanes per row: 8 below K = 6144 (64 rows, 40 KB of K = 2560 weights
         // per workgroup), 16 above (32 rows, 54 KB at K = 6912).  Few, large
         // workgroups repeat the activation quantisation fewer times; on the
