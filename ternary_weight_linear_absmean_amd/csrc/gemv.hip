@@ -186,7 +186,8 @@ hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
 // ---------------------------------------------------------------------------
 // Fused decode kernel: per-token absmax int8 quantisation folded into the
 // GEMV, for several independent BitLinears in one launch.  Workgroups are
-// dealt to jobs in order (job j owns workgroups [wg_begin_j, wg_begin_j+1)).
+// dealt to the jobs in order of decreasing K, so the longest run first (job
+// j of that order owns workgroups [wg_begin_j, wg_begin_j+1)).
 // A workgroup's waves have two roles:
 //   quantising waves (4) read the job's activation rows (L2-resident after
 //     the first workgroup) into LDS, form max |x| per token (counting up an
