@@ -78,6 +78,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K, int KC,
     float *__restrict__ Y, int32_t *__restrict__ acc_out) {
+    // every argument from the kernarg segment in one batch of scalar loads
+    // (one wait), not each batch where it is first used
+    asm volatile("" ::"s"(Xq), "s"(d), "s"(M), "s"(Wp), "s"(gamma), "s"(N), "s"(K), "s"(KC), "s"(Y), "s"(acc_out));
     constexpr int R = 64 / L;
     extern __shared__ uint4 xs[];                     // [MT][KC / 16], transposed groups
     const int tid = threadIdx.x;
@@ -90,11 +93,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int gpc = KC / 16;                           // 16-byte groups per staged row
     // Rows past N read the last row (in bounds) and are never stored.
     const uint4 *wrow = reinterpret_cast<const uint4 *>(Wp + (size_t)min(row, N - 1) * (K / 4));
-    // the epilogue's scales, loaded now rather than after the dot products
-    const float gam = scalar_load(gamma);
+    // the epilogue's scales, loaded now on the vector path: scalar loads
+    // would put their round trip (pointer, then value) in front of the
+    // weight loads, since every wait for a scalar load waits for all of them
+    const float gam = __hip_atomic_load(gamma, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float dv[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) dv[m] = m < mt ? scalar_load(d + m0 + m) : 0.0f;
+    for (int m = 0; m < MT; ++m)
+        dv[m] = m < mt ? __hip_atomic_load(d + m0 + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
 
     int acc[MT];
 #pragma unroll

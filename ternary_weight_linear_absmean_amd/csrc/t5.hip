@@ -123,6 +123,9 @@ __global__ __launch_bounds__(kT5Threads) void gemv_t5_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wt5, const float *__restrict__ gamma, int N, int K, int RB,
     float *__restrict__ Y, int32_t *__restrict__ acc_out) {
+    // every argument from the kernarg segment in one batch of scalar loads
+    // (one wait), not each batch where it is first used
+    asm volatile("" ::"s"(Xq), "s"(d), "s"(M), "s"(Wt5), "s"(gamma), "s"(N), "s"(K), "s"(RB), "s"(Y), "s"(acc_out));
     constexpr int R = 64 / L;
     extern __shared__ uint4 xs[];                 // [MT][U][5]
     __shared__ int sx[MT];
@@ -134,10 +137,14 @@ __global__ __launch_bounds__(kT5Threads) void gemv_t5_kernel(
     const int U = RB / 16;
     // Rows past N read the last row (in bounds) and are never stored.
     const uint4 *wrow = reinterpret_cast<const uint4 *>(Wt5 + (size_t)min(row, N - 1) * RB);
-    const float gam = scalar_load(gamma);
+    // the epilogue's scales, loaded now on the vector path: scalar loads
+    // would put their round trip (pointer, then value) in front of the
+    // weight loads, since every wait for a scalar load waits for all of them
+    const float gam = __hip_atomic_load(gamma, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float dv[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) dv[m] = m < mt ? scalar_load(d + m0 + m) : 0.0f;
+    for (int m = 0; m < MT; ++m)
+        dv[m] = m < mt ? __hip_atomic_load(d + m0 + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
 
     uint4 w[kT5InFlight];
 #pragma unroll
