@@ -468,3 +468,37 @@ def test_fused_zero_rows_job_still_quantises(gpu):
     Xq_ref, d_ref = _ref_act(X)
     assert np.array_equal(out[0]["Xq"].cpu().numpy(), Xq_ref)
     assert out[0]["Y"].shape == (1, 0)
+
+
+def test_fused_mixed_order_with_quantise_only_job(gpu):
+    """The launch orders the jobs by decreasing K (stable); a quantise-only
+    job (no rows) between product jobs of equal and unequal K keeps its own
+    Xq and d, and every product job its own Y."""
+    specs = [(2560, 100), (6912, 0), (1024, 33), (2560, 64), (6912, 40)]
+    jobs, refs = [], []
+    for i, (K, N) in enumerate(specs):
+        if N == 0:
+            X = workloads.activations(workloads.generator(950 + i), 1, K)
+            job = dict(X=X.cuda(), Wp=torch.zeros(0, K // 4, dtype=torch.uint8, device="cuda"),
+                       gamma=torch.ones(1, device="cuda"), Xq=None, d=None)
+            refs.append((X, None))
+        else:
+            W, X = workloads.bitlinear_problem(950 + i, 1, K, N, dtype=torch.bfloat16)
+            Wp, g = _gpu_weight(gpu, W)
+            job = dict(X=X.cuda(), Wp=Wp, gamma=g, Xq=None, d=None)
+            refs.append((X, W))
+        jobs.append(job)
+    out = gpu.bitlinear_gemv_fused(jobs)
+    torch.cuda.synchronize()
+    for (X, W), j in zip(refs, out):
+        K = X.shape[1]
+        Xq_ref, d_ref = _ref_act(X)
+        assert np.array_equal(j["Xq"].cpu().numpy(), Xq_ref)
+        assert np.array_equal(_f32_bits(j["d"].cpu().numpy()), _f32_bits(d_ref))
+        if W is None:
+            assert j["Y"].shape == (1, 0)
+            continue
+        Wp_ref, g_ref = oracle.quantize_weight(W.numpy())
+        acc_ref, Y_ref = oracle.bitlinear(Xq_ref, d_ref, Wp_ref, g_ref, K)
+        _assert_y_bits(j["Y"].cpu().numpy(), acc_ref, d_ref, g_ref)
+        _assert_close(j["Y"].cpu().numpy(), Y_ref)
