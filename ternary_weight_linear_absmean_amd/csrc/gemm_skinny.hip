@@ -1,27 +1,10 @@
-// gemm_skinny.hip -- W1.58A8 product for a few tokens (M < 128) on int8
-// MFMA, reading every packed weight once.
+// gemm_skinny.hip -- W1.58A8 product for a few tokens (M < 128, K <= 8192) on
+// int8 MFMA, each workgroup reading its weight rows once.
 //
 // Same product as gemm.hip (the technical-report copy's GPU端 pack / load /
 // unpack / compute, int32 accumulation, rescale fl(float(acc) * fl(gamma d))),
-// laid out for small M, where the weights dominate the bytes and there are
-// too few token tiles to fill the chip:
-//
-//   * a workgroup (4 waves) owns 32 weight rows -- one 32-column block of Y --
-//     for every token: MB blocks of 32 tokens, the rows past M are zero;
-//   * K is cut into chunks of 512; wave w takes the chunk's 128-wide quarter
-//     w, so a lane needs one 16-byte unit of its row per chunk: lane
-//     (r = lane % 32, h = lane / 32) reads bytes [32 q + 16 h, +16) of row r
-//     for quarter q.  Every unit of the workgroup is requested at kernel
-//     start (K <= 8192: at most 16 per lane), so the whole weight stream is in
-//     flight at once;
-//   * the tokens' codes of each chunk are staged in LDS (transposed 16-byte
-//     groups, double-buffered, loaded one chunk ahead);
-//   * k-step t of quarter q takes dword t of each lane's unit, i.e. weights
-//     k in [128 q + 64 h + 16 t, +16) on lane half h; the matching activation
-//     group (8 w + 4 h + t of the chunk) is the A operand of
-//     v_mfma_i32_32x32x32_i8, so each MFMA sums the 32 k of its two halves;
-//   * the four waves' int32 partial sums (disjoint k) are added through LDS
-//     and the epilogue rescales and stores the 32 x M block.
+// laid out for small M, where the packed weights are most of the bytes and a
+// launch is bound by load latency rather than by MFMA work.
 // Integer sums are exact, so the result does not depend on how k is split.
 #include "device_common.h"
 #include "launch.h"
@@ -30,12 +13,7 @@ namespace bl {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr int kSkThreads = 256;
-constexpr int kSkChunk = 512;                     // k per chunk: 4 waves x 128
-constexpr int kSkMaxChunks = 16;                  // K <= 8192
-constexpr int kSkPitch = kSkChunk / 16 + 1;       // uint4 per staged token row (+1 pad)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4i as_v4i(uint4 v) {
     v4i r;
@@ -43,350 +21,197 @@ __device__ __forceinline__ v4i as_v4i(uint4 v) {
     return r;
 }
 
-// Activation groups of one chunk: token rows 32 MB, 32 groups of 16 codes.
-// Thread tid stages groups e = tid + 256 i (token e / 32, group e % 32).
-template <int MB>
-__device__ __forceinline__ void load_chunk(uint4 (&a)[MB * 4], const int8_t *__restrict__ Xq, int M,
-                                           int K, int k0, int tid) {
-#pragma unroll
-    for (int i = 0; i < MB * 4; ++i) {
-        const int e = tid + kSkThreads * i;
-        const int tk = e >> 5, k = k0 + 16 * (e & 31);
-        // groups past M or K are zeros (whole waves of them issue no load)
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (tk < M && k < K) v = *reinterpret_cast<const uint4 *>(Xq + (size_t)tk * K + k);
-        a[i] = v;
-    }
-}
-template <int MB>
-__device__ __forceinline__ void store_chunk(const uint4 (&a)[MB * 4], uint4 *buf, int tid) {
-#pragma unroll
-    for (int i = 0; i < MB * 4; ++i) {
-        const int e = tid + kSkThreads * i;
-        buf[(e >> 5) * kSkPitch + (e & 31)] = transpose16(a[i]);
-    }
-}
+// A workgroup owns 16 tokens (one token block) and 16 RB weight rows,
+// K <= 2048 NR.  Its waves have two roles, as in the fused one-token GEMV:
+//   * four staging waves copy the block's 16 code rows into LDS as
+//     transposed 16-byte groups, in rounds of 2048 k (128 groups), and count
+//     up the round's LDS word after each round; all their loads are issued
+//     at once;
+//   * eight compute waves request every packed-weight unit they use at
+//     kernel start, then per round wait for the count and run the MFMAs.
+// A wave's vector loads complete in issue order, so activation loads that a
+// wave issues behind its weight requests wait for the whole weight stream;
+// with the roles split, the codes reach LDS as the first weights land.
+// (Kernels that staged the codes behind their own weight loads took 7.3 /
+// 9.7 / 14.4 us at M = 8 / 32 / 64, K6912 -> N2560, against 5.5 / 6.4 / 8.6.)
+//
+// k layout: unit u of a row is weights [64 u, +64), packed bytes [16 u, +16).
+// Compute wave cw takes the unit quads qd = cw + 8 rho (rho = round); lane
+// (r = lane % 16, g = lane / 16) holds unit 4 qd + g of row r of each row
+// block and feeds its dword t to MFMA step t: weights k in
+// [256 qd + 64 g + 16 t, +16) against activation group 16 qd + 4 g + t of
+// token r (the A operand of v_mfma_i32_16x16x64_i8).  Codes past M or past
+// K are staged as zeros (each staging load's buffer range is one token row),
+// so the weight units past K may hold anything: their products are zero.
+// Each token block re-reads the row group's weights; the grid puts all
+// token blocks of a row group on one XCD (workgroup x runs on XCD x % 8), so
+// those re-reads meet one L2.
+constexpr int kFwStageThreads = 256;              // four staging waves
+constexpr int kFwComputeWaves = 8;
+constexpr int kFwThreads = kFwStageThreads + 64 * kFwComputeWaves;
+constexpr int kFwRoundGroups = 128;               // 16-code groups per round: 8 waves x 4 units x 4
+constexpr int kFwMaxRounds = 4;                   // K <= 8192
+// Buffer resource word 3 for raw (untyped, unswizzled) loads: 32-bit data
+// format; a load at or past num_records bytes returns zeros.
+constexpr int kRawBufferWord3 = 0x00020000;
 
-template <int MB>
-__global__ __launch_bounds__(kSkThreads) void gemm_skinny_kernel(
+template <int RB, int NR>
+__global__ __launch_bounds__(kFwThreads) void gemm_few_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
     const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
-    float *__restrict__ Y, int32_t *__restrict__ acc_out) {
-    constexpr int kStage = 32 * MB * kSkPitch;                  // uint4 per chunk buffer
-    __shared__ uint4 As[2 * kStage];
-    __shared__ float cS[32 * MB];                               // fl(gamma * d[token])
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * 32;
-    const int nch = (K + kSkChunk - 1) / kSkChunk;
-    const int KB = K / 4;
+    float *__restrict__ Y, int32_t *__restrict__ acc_out, int ntb, int nrg) {
+    constexpr int P = kFwRoundGroups * NR + 1;             // uint4 per staged token row (odd)
+    constexpr int kXsU4 = 16 * P;
+    constexpr int kRedU4 = kFwComputeWaves * RB * 4 * 64 / 4;   // int [8][RB][4][64]
+    __shared__ uint4 xs[kXsU4 > kRedU4 ? kXsU4 : kRedU4];
+    __shared__ float cS[16];                               // fl(gamma * d[token])
+    // staging waves past each round, one word per round: a single count
+    // could reach 4 (rho + 1) while a slow wave is still in round rho
+    __shared__ unsigned n_staged[NR];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int slot = (int)blockIdx.x >> 3;
+    const int tb = slot % ntb, rg = (slot / ntb) * 8 + ((int)blockIdx.x & 7);
+    if (rg >= nrg)
+        return;                                            // the whole workgroup, before any barrier
+    const int m0 = 16 * tb, mt = min(16, M - m0);
+    const int n0 = 16 * RB * rg;
+    if (tid < NR)
+        n_staged[tid] = 0u;
+    __syncthreads();                                       // nothing is in flight yet
 
-    // 1. every packed-weight unit of this lane, requested before anything else
-    const uint8_t *wrow = Wp + (size_t)min(n0 + (lane & 31), N - 1) * KB;
-    uint4 w[kSkMaxChunks];
+    v4i acc[RB];
 #pragma unroll
-    for (int c = 0; c < kSkMaxChunks; ++c) {
-        if (c < nch) {
-            const int q = 4 * c + wave;                          // 128-wide quarter
-            const int off = 32 * q + 16 * (lane >> 5);           // byte offset in the row
-            const bool ok = off < KB;                            // K % 64 == 0: whole units
-            const uint4 v = *reinterpret_cast<const uint4 *>(wrow + min(off, KB - 16));
-            w[c] = ok ? v : make_uint4(0u, 0u, 0u, 0u);         // code 0 = weight 0
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = v4i{0, 0, 0, 0};
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (__builtin_expect(wave < kFwStageThreads / 64, 1)) {
+        // ---- staging waves: load i of a round covers 64 consecutive groups
+        //      of token (tid / 128) + 2 i, wave-uniform, so each load's buffer
+        //      range is that token's row (empty past M)
+        const int half = __builtin_amdgcn_readfirstlane(tid >> 7), e = tid & 127;
+        __amdgpu_buffer_rsrc_t rs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = half + 2 * i;
+            rs[i] = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<int8_t *>(Xq + (size_t)(m0 + min(t, mt - 1)) * K), (short)0,
+                t < mt ? K : 0, kRawBufferWord3);
         }
-    }
-
-    // 2. row factors and the first activation chunks: PF chunks are held in
-    //    registers ahead of the one in LDS (two where registers allow)
-    constexpr int PF = MB <= 2 ? 2 : 1;
-    const float g = scalar_load(gamma);
-    if (tid < 32 * MB) cS[tid] = tid < M ? __fmul_rn(g, d[tid]) : 0.0f;
-    uint4 a[PF][MB * 4];
-    load_chunk<MB>(a[0], Xq, M, K, 0, tid);
-    if constexpr (PF == 2) {
-        if (nch > 1) load_chunk<MB>(a[1], Xq, M, K, kSkChunk, tid);
-    }
-    store_chunk<MB>(a[0], As, tid);
-    if (nch > PF) load_chunk<MB>(a[0], Xq, M, K, PF * kSkChunk, tid);
-    __syncthreads();
-
-    v16i acc[MB];
+        uint4 a[NR][8];                                    // round-major: round 0 lands first
 #pragma unroll
-    for (int b = 0; b < MB; ++b) acc[b] = v16i{};
-
-    // 3. chunk loop: MFMAs on chunk c while chunks c + 1 .. c + PF sit in
-    //    registers; register set (c + 1) % PF holds chunk c + 1
+        for (int rho = 0; rho < NR; ++rho) {
 #pragma unroll
-    for (int c = 0; c < kSkMaxChunks; ++c) {
-        if (c < nch) {
-            const uint4 *A = As + (c & 1) * kStage;
-            const uint32_t dws[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+            for (int i = 0; i < 8; ++i) {
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs[i], 16 * (kFwRoundGroups * rho + e), 0, 0);
+                a[rho][i] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+            __builtin_amdgcn_sched_barrier(0);             // keep the rounds in issue order
+        }
+#pragma unroll
+        for (int rho = 0; rho < NR; ++rho) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                xs[(half + 2 * i) * P + kFwRoundGroups * rho + e] = transpose16(a[rho][i]);
+            // this wave's groups of the round in LDS before the count
+            if (lane == 0)
+                __hip_atomic_fetch_add(&n_staged[rho], 1u, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        // the row factors, needed only by the epilogue (behind the final barrier)
+        if (tid < 16)
+            cS[tid] = tid < mt ? __fmul_rn(scalar_load(gamma), d[m0 + tid]) : 0.0f;
+    } else {
+        // ---- compute waves: every unit requested at once, round 0's first
+        const int cw = wave - kFwStageThreads / 64;
+        const int r = lane & 15, g = lane >> 4;
+        const int U = K >> 6, KB = K >> 2;
+        uint4 w[NR][RB];
+#pragma unroll
+        for (int rho = 0; rho < NR; ++rho) {
+            const int u = min(4 * (cw + 8 * rho) + g, U - 1);   // past K: any unit (zero codes)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int row = min(n0 + 16 * rb + r, N - 1);    // past N: discarded outputs
+                w[rho][rb] = *reinterpret_cast<const uint4 *>(Wp + (size_t)row * KB + 16 * u);
+            }
+        }
+#pragma unroll
+        for (int rho = 0; rho < NR; ++rho) {
+            const int qd = cw + 8 * rho;
+            if (4 * qd >= U)
+                break;                                     // wave-uniform: no unit left
+            while (__hip_atomic_load(&n_staged[rho], __ATOMIC_ACQUIRE,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP) < 4u)
+                __builtin_amdgcn_s_sleep(1);
+            const uint4 *A = xs + r * P + 16 * qd + 4 * g;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                uint4 bv;
-                unpack16(dws[t], bv.x, bv.y, bv.z, bv.w);
-                const v4i bf = as_v4i(bv);
-                const int grp = 8 * wave + 4 * (lane >> 5) + t;
+                const v4i af = as_v4i(A[t]);
 #pragma unroll
-                for (int b = 0; b < MB; ++b) {
-                    const v4i af = as_v4i(A[(32 * b + (lane & 31)) * kSkPitch + grp]);
-                    acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, acc[b], 0, 0, 0);
+                for (int rb = 0; rb < RB; ++rb) {
+                    const uint32_t dw = t == 0 ? w[rho][rb].x : t == 1 ? w[rho][rb].y
+                                      : t == 2 ? w[rho][rb].z : w[rho][rb].w;
+                    uint4 bv;
+                    unpack16(dw, bv.x, bv.y, bv.z, bv.w);
+                    acc[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, as_v4i(bv), acc[rb], 0, 0, 0);
                 }
             }
-            if (c + 1 < nch) {
-                store_chunk<MB>(a[(c + 1) % PF], As + ((c + 1) & 1) * kStage, tid);
-                if (c + 1 + PF < nch)
-                    load_chunk<MB>(a[(c + 1) % PF], Xq, M, K, (c + 1 + PF) * kSkChunk, tid);
-            }
-            __syncthreads();
         }
     }
 
-    // 4. add the four waves' partial sums through LDS (the stages are free now)
-    int *red = reinterpret_cast<int *>(As);                     // [4][MB][16][64]
+    // the eight compute waves' sums (disjoint k) through LDS, then the
+    // 16 RB x mt outputs, a token's columns on consecutive threads
+    __syncthreads();                                       // every wave is done with the codes
+    int *red = reinterpret_cast<int *>(xs);
+    if (wave >= kFwStageThreads / 64) {
+        const int cw = wave - kFwStageThreads / 64;
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[((wave * MB + b) * 16 + r) * 64 + lane] = acc[b][r];
+            for (int v = 0; v < 4; ++v) red[((cw * RB + rb) * 4 + v) * 64 + lane] = acc[rb][v];
+    }
     __syncthreads();
+    for (int o = tid; o < 256 * RB; o += kFwThreads) {
+        const int tok = o / (16 * RB), c = o % (16 * RB);
+        const int rb = c >> 4, l = 16 * (tok >> 2) + (c & 15), v = tok & 3;
+        int sum = 0;
 #pragma unroll
-    for (int i = 0; i < MB * 4; ++i) {
-        const int e = tid + kSkThreads * i;                      // (b, r, l) = e / 1024, ...
-        const int b = e >> 10, r = (e >> 6) & 15, l = e & 63;
-        int s = 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s += red[((v * MB + b) * 16 + r) * 64 + l];
-        const int lt = 32 * b + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);   // token in the block
-        const int col = n0 + (l & 31);
-        if (lt < M && col < N) {
-            const size_t o = (size_t)lt * N + col;
-            Y[o] = rescale(s, cS[lt]);
-            if (acc_out) acc_out[o] = s;
+        for (int cw = 0; cw < kFwComputeWaves; ++cw) sum += red[((cw * RB + rb) * 4 + v) * 64 + l];
+        const int col = n0 + c;
+        if (tok < mt && col < N) {
+            const size_t off = (size_t)(m0 + tok) * N + col;
+            Y[off] = rescale(sum, cS[tok]);
+            if (acc_out) acc_out[off] = sum;
         }
     }
 }
 
-// Resident variant for M * K <= 64 KB (e.g. up to 9 tokens at K = 6912):
-// every activation group is requested together with the weights at kernel
-// start and staged once, [M][K / 16 + 1] groups in LDS, so the chunk loop
-// runs with no barrier.  A lanes of token rows past M take zeros; groups
-// past K in the last chunk meet zero weights (and stay inside the array,
-// see res_fits).
-constexpr int kResGroups = 4096;                 // 64 KB of LDS
-constexpr int kResLoads = kResGroups / kSkThreads;
-
-__global__ __launch_bounds__(kSkThreads) void gemm_skinny_res_kernel(
-    const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
-    const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
-    float *__restrict__ Y, int32_t *__restrict__ acc_out) {
-    __shared__ uint4 As[kResGroups];
-    __shared__ float cS[32];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * 32;
-    const int nch = (K + kSkChunk - 1) / kSkChunk;
-    const int KB = K / 4, G = K / 16, P = G + 1;
-
-    const uint8_t *wrow = Wp + (size_t)min(n0 + (lane & 31), N - 1) * KB;
-    uint4 w[kSkMaxChunks];
-#pragma unroll
-    for (int c = 0; c < kSkMaxChunks; ++c) {
-        if (c < nch) {
-            const int off = 32 * (4 * c + wave) + 16 * (lane >> 5);
-            const uint4 v = *reinterpret_cast<const uint4 *>(wrow + min(off, KB - 16));
-            w[c] = off < KB ? v : make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-    const int total = M * G;
-    uint4 a[kResLoads];
-#pragma unroll
-    for (int i = 0; i < kResLoads; ++i) {
-        const int e = tid + kSkThreads * i;
-        a[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (e < total) {
-            const int tk = e / G, grp = e - tk * G;
-            a[i] = *reinterpret_cast<const uint4 *>(Xq + (size_t)tk * K + 16 * grp);
-        }
-    }
-    const float g = scalar_load(gamma);
-    if (tid < 32) cS[tid] = tid < M ? __fmul_rn(g, d[tid]) : 0.0f;
-#pragma unroll
-    for (int i = 0; i < kResLoads; ++i) {
-        const int e = tid + kSkThreads * i;
-        if (e < total) {
-            const int tk = e / G, grp = e - tk * G;
-            As[tk * P + grp] = transpose16(a[i]);
-        }
-    }
-    __syncthreads();
-
-    v16i acc = v16i{};
-    const int m = lane & 31;
-    const bool live = m < M;
-#pragma unroll
-    for (int c = 0; c < kSkMaxChunks; ++c) {
-        if (c < nch) {
-            const uint32_t dws[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                uint4 bv;
-                unpack16(dws[t], bv.x, bv.y, bv.z, bv.w);
-                const int grp = 32 * c + 8 * wave + 4 * (lane >> 5) + t;
-                const uint4 av = live ? As[m * P + grp] : make_uint4(0u, 0u, 0u, 0u);
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_v4i(av), as_v4i(bv), acc, 0, 0, 0);
-            }
-        }
-    }
-
-    __syncthreads();                              // every wave is done reading As
-    int *red = reinterpret_cast<int *>(As);       // [4][16][64]
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = tid + kSkThreads * i;
-        const int r = e >> 6, l = e & 63;
-        const int s = red[r * 64 + l] + red[(16 + r) * 64 + l] + red[(32 + r) * 64 + l] +
-                      red[(48 + r) * 64 + l];
-        const int lt = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-        const int col = n0 + (l & 31);
-        if (lt < M && col < N) {
-            const size_t o = (size_t)lt * N + col;
-            Y[o] = rescale(s, cS[lt]);
-            if (acc_out) acc_out[o] = s;
-        }
-    }
+template <int RB, int NR>
+void launch_few(const int8_t *Xq, const float *d, int M, const uint8_t *Wp, const float *gamma,
+                int N, int K, float *Y, int32_t *acc, hipStream_t s) {
+    const int ntb = (M + 15) / 16, nrg = (N + 16 * RB - 1) / (16 * RB);
+    const dim3 grid(8 * ntb * ((nrg + 7) / 8));
+    hipLaunchKernelGGL((gemm_few_kernel<RB, NR>), grid, dim3(kFwThreads), 0, s, Xq, d, M, Wp,
+                       gamma, N, K, Y, acc, ntb, nrg);
 }
 
-// Narrow-N variant on v_mfma_i32_16x16x64_i8: 16 weight rows per workgroup,
-// so N = 2560 spreads over 160 workgroups instead of 80 (each CU streams half
-// as many bytes).  Chunks are 1024 wide and wave w takes the 256-wide quarter
-// w: lane (r = lane % 16, g = lane / 16) reads the 64 weights
-// [kq + 64 g, +64) of row r as one 16-byte unit and uses its dword t in
-// MFMA step t (k in [kq + 64 g + 16 t, +16) on lane group g, kq the quarter's
-// first k); the A operand of token m on lane group g is activation group
-// kq / 16 + 4 g + t.  Tokens come in MB blocks of 16.
-constexpr int kS16Chunk = 1024;
-constexpr int kS16MaxChunks = 8;                  // K <= 8192
-constexpr int kS16Pitch = kS16Chunk / 16 + 1;     // uint4 per staged token row (+1 pad)
-
-template <int MB>
-__device__ __forceinline__ void load_chunk16(uint4 (&a)[MB * 4], const int8_t *__restrict__ Xq,
-                                             int M, int K, int k0, int tid) {
-#pragma unroll
-    for (int i = 0; i < MB * 4; ++i) {
-        const int e = tid + kSkThreads * i;                      // token e / 64, group e % 64
-        const int tk = e >> 6, k = k0 + 16 * (e & 63);
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (tk < M && k < K) v = *reinterpret_cast<const uint4 *>(Xq + (size_t)tk * K + k);
-        a[i] = v;
+template <int NR>
+void launch_few_rb(int rb, const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
+                   const float *gamma, int N, int K, float *Y, int32_t *acc, hipStream_t s) {
+    if (rb == 1) launch_few<1, NR>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    else if (rb == 2) launch_few<2, NR>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    else if constexpr (NR <= 2) {
+        if (rb == 4) launch_few<4, NR>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+        else launch_few<8, NR>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
+    } else {
+        launch_few<4, NR>(Xq, d, M, Wp, gamma, N, K, Y, acc, s);
     }
 }
-template <int MB>
-__device__ __forceinline__ void store_chunk16(const uint4 (&a)[MB * 4], uint4 *buf, int tid) {
-#pragma unroll
-    for (int i = 0; i < MB * 4; ++i) {
-        const int e = tid + kSkThreads * i;
-        buf[(e >> 6) * kS16Pitch + (e & 63)] = transpose16(a[i]);
-    }
-}
-
-template <int MB>
-__global__ __launch_bounds__(kSkThreads) void gemm_skinny16_kernel(
-    const int8_t *__restrict__ Xq, const float *__restrict__ d, int M,
-    const uint8_t *__restrict__ Wp, const float *__restrict__ gamma, int N, int K,
-    float *__restrict__ Y, int32_t *__restrict__ acc_out) {
-    constexpr int kStage = 16 * MB * kS16Pitch;
-    __shared__ uint4 As[2 * kStage];
-    __shared__ float cS[16 * MB];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * 16;
-    const int nch = (K + kS16Chunk - 1) / kS16Chunk;
-    const int KB = K / 4;
-
-    const uint8_t *wrow = Wp + (size_t)min(n0 + (lane & 15), N - 1) * KB;
-    uint4 w[kS16MaxChunks];
-#pragma unroll
-    for (int c = 0; c < kS16MaxChunks; ++c) {
-        if (c < nch) {
-            const int off = 256 * c + 64 * wave + 16 * (lane >> 4);   // bytes: quarter + unit
-            const uint4 v = *reinterpret_cast<const uint4 *>(wrow + min(off, KB - 16));
-            w[c] = off < KB ? v : make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-
-    constexpr int PF = MB <= 2 ? 2 : 1;
-    const float g = scalar_load(gamma);
-    if (tid < 16 * MB) cS[tid] = tid < M ? __fmul_rn(g, d[tid]) : 0.0f;
-    uint4 a[PF][MB * 4];
-    load_chunk16<MB>(a[0], Xq, M, K, 0, tid);
-    if constexpr (PF == 2) {
-        if (nch > 1) load_chunk16<MB>(a[1], Xq, M, K, kS16Chunk, tid);
-    }
-    store_chunk16<MB>(a[0], As, tid);
-    if (nch > PF) load_chunk16<MB>(a[0], Xq, M, K, PF * kS16Chunk, tid);
-    __syncthreads();
-
-    v4i acc[MB];
-#pragma unroll
-    for (int b = 0; b < MB; ++b) acc[b] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int c = 0; c < kS16MaxChunks; ++c) {
-        if (c < nch) {
-            const uint4 *A = As + (c & 1) * kStage;
-            const uint32_t dws[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                uint4 bv;
-                unpack16(dws[t], bv.x, bv.y, bv.z, bv.w);
-                const v4i bf = as_v4i(bv);
-                const int grp = 16 * wave + 4 * (lane >> 4) + t;
-#pragma unroll
-                for (int b = 0; b < MB; ++b) {
-                    const v4i af = as_v4i(A[(16 * b + (lane & 15)) * kS16Pitch + grp]);
-                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[b], 0, 0, 0);
-                }
-            }
-            if (c + 1 < nch) {
-                store_chunk16<MB>(a[(c + 1) % PF], As + ((c + 1) & 1) * kStage, tid);
-                if (c + 1 + PF < nch)
-                    load_chunk16<MB>(a[(c + 1) % PF], Xq, M, K, (c + 1 + PF) * kS16Chunk, tid);
-            }
-            __syncthreads();
-        }
-    }
-
-    // the four waves' sums: [4][MB][4][64] through LDS, then 16 x M outputs
-    int *red = reinterpret_cast<int *>(As);
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[((wave * MB + b) * 4 + r) * 64 + lane] = acc[b][r];
-    __syncthreads();
-    if (tid < MB * 64) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int b = tid >> 6, l = tid & 63;
-            int sum = 0;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sum += red[((v * MB + b) * 4 + r) * 64 + l];
-            const int lt = 16 * b + 4 * (l >> 4) + r;            // token
-            const int col = n0 + (l & 15);
-            if (lt < M && col < N) {
-                const size_t o = (size_t)lt * N + col;
-                Y[o] = rescale(sum, cS[lt]);
-                if (acc_out) acc_out[o] = sum;
-            }
-        }
-    }
-}
-
-// The resident layout holds M rows of K / 16 + 1 groups, and the last chunk
-// may read up to 31 groups past a row's end: M (K / 16 + 1) + 32 <= 4096.
-bool res_fits(int M, int K) { return M <= 32 && M * (K / 16 + 1) + 32 <= kResGroups; }
 
 }  // namespace
 
 bool gemm_skinny_fits(int M, int K) {
-    return M >= 1 && M < 128 && K >= 64 && K <= kSkMaxChunks * kSkChunk;
+    return M >= 1 && M < 128 && K >= 64 && K <= kFwMaxRounds * 16 * kFwRoundGroups;
 }
 
 hipError_t launch_gemm_skinny(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
@@ -394,33 +219,22 @@ hipError_t launch_gemm_skinny(const int8_t *Xq, const float *d, int M, const uin
                               hipStream_t s) {
     if (M == 0 || N == 0)
         return hipSuccess;
-    // Narrow N: 16-row workgroups when 32-row ones would leave most CUs idle.
-    if (N <= 4096 && M <= 64) {
-        const dim3 grid16((N + 15) / 16);
-        if (M <= 16)
-            hipLaunchKernelGGL(gemm_skinny16_kernel<1>, grid16, dim3(kSkThreads), 0, s, Xq, d, M, Wp,
-                               gamma, N, K, Y, acc);
-        else if (M <= 32)
-            hipLaunchKernelGGL(gemm_skinny16_kernel<2>, grid16, dim3(kSkThreads), 0, s, Xq, d, M, Wp,
-                               gamma, N, K, Y, acc);
-        else
-            hipLaunchKernelGGL(gemm_skinny16_kernel<4>, grid16, dim3(kSkThreads), 0, s, Xq, d, M, Wp,
-                               gamma, N, K, Y, acc);
-        return hipGetLastError();
+    // Rows per workgroup 16 RB: the fewest that keep the grid within one
+    // workgroup per CU (at most 256), capped so that a lane's weight units
+    // (RB per round) fit in 64 registers.  Measured at K2560 -> N6912, M = 8:
+    // 5.2 us; half the rows and two workgroups per CU, 6.0; twice the rows
+    // (at most 128 workgroups), 6.0.
+    const int nr = (K + 16 * kFwRoundGroups - 1) / (16 * kFwRoundGroups);   // rounds of 2048 k, <= 4
+    const int ntb = (M + 15) / 16;
+    const int rb_max = nr <= 2 ? 8 : 4;
+    int rb = 1;
+    while (rb < rb_max && ntb * ((N + 16 * rb - 1) / (16 * rb)) > 256) rb *= 2;
+    switch (nr) {
+    case 1: launch_few_rb<1>(rb, Xq, d, M, Wp, gamma, N, K, Y, acc, s); break;
+    case 2: launch_few_rb<2>(rb, Xq, d, M, Wp, gamma, N, K, Y, acc, s); break;
+    case 3: launch_few_rb<3>(rb, Xq, d, M, Wp, gamma, N, K, Y, acc, s); break;
+    default: launch_few_rb<4>(rb, Xq, d, M, Wp, gamma, N, K, Y, acc, s); break;
     }
-    const dim3 grid((N + 31) / 32);
-    if (res_fits(M, K))
-        hipLaunchKernelGGL(gemm_skinny_res_kernel, grid, dim3(kSkThreads), 0, s, Xq, d, M, Wp, gamma,
-                           N, K, Y, acc);
-    else if (M <= 32)
-        hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(kSkThreads), 0, s, Xq, d, M, Wp, gamma,
-                           N, K, Y, acc);
-    else if (M <= 64)
-        hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(kSkThreads), 0, s, Xq, d, M, Wp, gamma,
-                           N, K, Y, acc);
-    else
-        hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(kSkThreads), 0, s, Xq, d, M, Wp, gamma,
-                           N, K, Y, acc);
     return hipGetLastError();
 }
 

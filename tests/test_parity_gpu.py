@@ -194,19 +194,25 @@ def test_gemv_ragged(gpu, M, K, N):
 
 
 @pytest.mark.parametrize("call,M,K,N", [
-    # N <= 4096, M <= 64: 16-row workgroups (16x16x64), token blocks of 16
-    ("bitlinear_gemm", 1, 6912, 100),     # one block, 7 chunks (the last 768 wide)
-    ("bitlinear_gemm", 17, 6912, 65),     # two blocks
-    ("bitlinear_gemm", 33, 576, 97),      # four blocks; one chunk of 576
-    ("bitlinear_gemv", 3, 320, 641),      # v_dot4 hands over to the MFMA kernels at M = 3
-    ("bitlinear_gemv", 64, 8192, 50),     # the largest K the few-token kernels take
-    # wider N, or M > 64: 32-row workgroups (32x32x32), token blocks of 32
-    ("bitlinear_gemm", 8, 6912, 4160),    # codes resident in LDS (M * K <= 64 KB)
-    ("bitlinear_gemm", 9, 6912, 4110),    # the largest resident case at K = 6912
-    ("bitlinear_gemm", 20, 2560, 4200),   # chunked, one block, chunks two ahead
-    ("bitlinear_gemm", 40, 576, 4200),    # two blocks; last chunk 64 wide
-    ("bitlinear_gemm", 100, 8192, 40),    # four blocks (M > 64), one chunk ahead
-    ("bitlinear_gemm", 127, 64, 33),      # one partial chunk, ragged N
+    # the role-split MFMA kernel (M < 128, K <= 8192): rounds of 2048 k,
+    # 16-token blocks, 16 RB weight rows per workgroup
+    ("bitlinear_gemm", 1, 6912, 100),     # one token; four rounds, the last partial
+    ("bitlinear_gemm", 17, 6912, 65),     # two token blocks, the second with one token
+    ("bitlinear_gemm", 33, 576, 97),      # three blocks; one partial round
+    ("bitlinear_gemv", 3, 320, 641),      # v_dot4 hands over to the MFMA kernel at M = 3
+    ("bitlinear_gemv", 64, 8192, 50),     # the largest K the kernel takes
+    ("bitlinear_gemm", 8, 6912, 4160),    # codes past M staged as zeros; RB = 2
+    ("bitlinear_gemm", 9, 6912, 4110),    # ragged N inside a row block
+    ("bitlinear_gemm", 20, 2560, 4200),   # two blocks, RB = 4 (grid past 256 otherwise)
+    ("bitlinear_gemm", 40, 576, 4200),    # a round of 36 groups
+    ("bitlinear_gemm", 100, 8192, 40),    # seven blocks, three row groups (the last ragged)
+    ("bitlinear_gemm", 127, 64, 33),      # one unit per row, eight blocks, ragged N
+    ("bitlinear_gemm", 16, 2048, 16),     # one round exactly, one workgroup
+    ("bitlinear_gemm", 5, 64, 300),       # one unit per row: only one lane group holds weights
+    ("bitlinear_gemm", 17, 2112, 4097),   # a 1-unit last round; two blocks; RB = 4, idle slots
+    ("bitlinear_gemv", 48, 4096, 1000),   # three token blocks (grid order by XCD)
+    ("bitlinear_gemm", 127, 6144, 2050),  # three rounds, eight blocks, RB capped at 4
+    ("bitlinear_gemv", 64, 2560, 6912),   # RB = 8
     # K past 8192: the earlier paths
     ("bitlinear_gemm", 5, 8256, 64),      # the 128 x 128 tile kernel
     ("bitlinear_gemv", 40, 8256, 30),     # v_dot4
