@@ -217,11 +217,16 @@ hipError_t launch_m(const int8_t *Xq, const float *d, int M, const uint8_t *Wp,
 // that waited for all twelve waves came about 1 us after the quantising
 // waves' own.
 // The arguments sit in the kernarg segment, which the waves read with scalar
-// loads whose every wait is a round trip to L2.  The layout keeps the chain
-// before the first weight and activation loads to two such trips: the header
-// (token count and each job's first workgroup, unused jobs at INT_MAX) in one
-// load, then the workgroup's job record (64 bytes) in one load.  Gamma is
-// read on the vector path instead, behind the weights.
+// loads whose every wait is a round trip to L2.  The token count and each
+// job's first workgroup come first, as separate scalar parameters, and the
+// library is built to preload the leading kernel arguments into SGPRs at wave
+// launch (gfx950 kernarg preload; on firmware without it, a prologue loads
+// them): the workgroup picks its job with no memory access and reads the job
+// record (64 bytes, on one 64-byte line) in one load, one round trip before
+// the first weight and activation loads (5.41-5.43 against 5.51-5.54 us per
+// step on the four decode shapes with the header loaded from the segment;
+// preloading the first job's pointers as well ran 5.45-5.47).  Gamma is read
+// on the vector path instead, behind the weights.
 struct FusedJob {
     const void *X;
     const uint8_t *Wp;
@@ -232,12 +237,11 @@ struct FusedJob {
     int N, K, dtype, lshift;          // lanes per row L = 1 << lshift
 };
 
-struct FusedArgs {
-    int M, pad;
-    int wg_begin[kMaxJobs];
+struct alignas(64) FusedArgs {                 // the job records; the header is passed before it
     FusedJob job[kMaxJobs];
 };
 static_assert(sizeof(FusedJob) == 64, "one 64-byte scalar load per job record");
+
 
 // 512 compute threads: every workgroup quantises its job's whole activation
 // row, so fewer, larger workgroups repeat that less; on the four 2B-class
@@ -302,16 +306,19 @@ __device__ __forceinline__ void unpack_x16(const uint4 (&raw)[4], int dtype, flo
 // matrix core, beside the other wave's unpacking; the c partials of a row
 // are added with shuffles.
 template <int MT, bool kMfma>
-__global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs args) {
+__global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(int Mtok, int b1, int b2, int b3, int b4, int b5, int b6, int b7,
+                                                                const FusedArgs args) {
+    // job t starts at workgroup b_t (job 0 at 0; unused jobs at INT_MAX)
+    const int wgb[kMaxJobs] = {0, b1, b2, b3, b4, b5, b6, b7};
     extern __shared__ uint4 xs[];   // [MT][K / 16] transposed code groups, then the raw activations
     __shared__ float red[kQWaves][MT];
     __shared__ unsigned n_amax, n_codes;        // quantising waves past each step
     int j = 0, jbegin = 0;
 #pragma unroll
     for (int t = 1; t < kMaxJobs; ++t)
-        if ((int)blockIdx.x >= args.wg_begin[t]) {
+        if ((int)blockIdx.x >= wgb[t]) {
             j = t;
-            jbegin = args.wg_begin[t];
+            jbegin = wgb[t];
         }
     const FusedJob jb = args.job[j];                // the record, copied by one load
     const int K = jb.K, N = jb.N, dtype = jb.dtype, lshift = jb.lshift;
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(kFThreads) void gemv_fused_kernel(const FusedArgs a
     const int lane = tid & 63;
     const int wg = (int)blockIdx.x - jbegin;
     const int m0 = blockIdx.y * MT;
-    const int mt = min(MT, args.M - m0);
+    const int mt = min(MT, Mtok - m0);
     const int U = K / 64;
     const int gpc = K / 16;
     if (tid == 0) {
@@ -633,18 +640,20 @@ hipError_t launch_gemv(const int8_t *Xq, const float *d, int M, const uint8_t *W
 namespace bl {
 namespace {
 template <int MT>
-hipError_t launch_fused_mt(const FusedArgs &a, int grid_x, int max_k, int max_es, hipStream_t s) {
-    const dim3 grid(grid_x, (a.M + MT - 1) / MT);
+hipError_t launch_fused_mt(const FusedArgs &a, const int *wgb, int M, int grid_x, int max_k, int max_es,
+                           hipStream_t s) {
+    const dim3 grid(grid_x, (M + MT - 1) / MT);
     hipLaunchKernelGGL((gemv_fused_kernel<MT, (MT <= BL_FUSED_MFMA_MAX_MT)>), grid, dim3(kFThreads),
-                       fused_lds_bytes(MT, max_k, max_es), s, a);
+                       fused_lds_bytes(MT, max_k, max_es), s, M, wgb[1], wgb[2], wgb[3], wgb[4], wgb[5],
+                       wgb[6], wgb[7], a);
     return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t s) {
     FusedArgs a = {};
-    a.M = M;
-    for (int j = 0; j < kMaxJobs; ++j) a.wg_begin[j] = INT_MAX;
+    int wg_begin[kMaxJobs];
+    for (int j = 0; j < kMaxJobs; ++j) wg_begin[j] = INT_MAX;
     int wg = 0, max_k = 0, max_es = 2;
     // Jobs in order of decreasing K (stable): the longest workgroups are
     // dispatched first.  Each job keeps its own outputs, so the order changes
@@ -669,7 +678,7 @@ hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t 
         f.lshift = BL_FUSED_LSHIFT;                     // tuning builds only
 #endif
         const int rows_per_wg = (kCThreads / 64) * (64 >> f.lshift);
-        a.wg_begin[j] = wg;
+        wg_begin[j] = wg;
         // a job with N == 0 still gets one workgroup when it must write Xq / d
         const int n_wg = f.N > 0 ? (f.N + rows_per_wg - 1) / rows_per_wg : ((f.Xq || f.d) ? 1 : 0);
         // A job with no output rows only quantises; its weight-row pointer
@@ -683,10 +692,10 @@ hipError_t launch_gemv_fused(const GemvJob *jobs, int count, int M, hipStream_t 
     }
     if (wg == 0)
         return hipSuccess;
-    if (M == 1) return launch_fused_mt<1>(a, wg, max_k, max_es, s);
-    if (M == 2) return launch_fused_mt<2>(a, wg, max_k, max_es, s);
-    if (M <= 4) return launch_fused_mt<4>(a, wg, max_k, max_es, s);
-    return launch_fused_mt<8>(a, wg, max_k, max_es, s);
+    if (M == 1) return launch_fused_mt<1>(a, wg_begin, M, wg, max_k, max_es, s);
+    if (M == 2) return launch_fused_mt<2>(a, wg_begin, M, wg, max_k, max_es, s);
+    if (M <= 4) return launch_fused_mt<4>(a, wg_begin, M, wg, max_k, max_es, s);
+    return launch_fused_mt<8>(a, wg_begin, M, wg, max_k, max_es, s);
 }
 
 }  // namespace bl
