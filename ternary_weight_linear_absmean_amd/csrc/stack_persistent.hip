@@ -410,9 +410,9 @@ __device__ __forceinline__ bool receive_p2(const PArgs &a, Smem &sm, int lg, flo
 __device__ __forceinline__ bool receive_p3(const PArgs &a, Smem &sm, int lg, const float *norm) {
     const int K = a.F;
     const int nj = (K / 2 + kR - 1) / kR;     // uniform
-    // The gains go through LDS (the loop after the poll reads them back in
-    // chunk order).  All loads are issued before any is used (buffer loads:
-    // past the end they give 0, never written).
+    // The gains go through LDS (each chunk's callback reads its own two back).
+    // All loads are issued before any is used (buffer loads: past the end
+    // they give 0, never written).
     if (norm) {
         const __amdgpu_buffer_rsrc_t rg = rsrc(norm, K * 4);
         v2u g[kNF];
@@ -435,24 +435,29 @@ __device__ __forceinline__ bool receive_p3(const PArgs &a, Smem &sm, int lg, con
                 *reinterpret_cast<float2 *>(sm.gain + 2 * c) = make_float2(1.0f, 1.0f);
         }
     }
+    // z = H g, max |z| and each chunk's H^2 are formed as the chunks arrive
+    // (in the emit callback, not in a pass over the staged row afterwards:
+    // 586-591 against 599-602 us per token); the fp64 sum then runs over the
+    // chunks in their fixed order, so every workgroup gets the same bits.
+    // (Parking the per-chunk terms in LDS instead of registers, which avoids
+    // a few register spills, measured 605-607 us.)
+    float am = 0.0f;
+    double ssc[kNF];
+#pragma unroll
+    for (int i = 0; i < kNF; ++i) ssc[i] = 0.0;
     const bool ok = receive<kNF, false>(a, slot(a, a.h, lg), tag_of(lg, 2), nullptr, 0u, K, K, Same{},
                                         [&](int c, const v4u &w, const v4u &) {
-        *reinterpret_cast<float2 *>(sm.vals + 2 * c) = halves(w);
+        const float2 hv = halves(w);
+        const float2 g = *reinterpret_cast<const float2 *>(sm.gain + 2 * c);
+        const float2 z = make_float2(__fmul_rn(hv.x, g.x), __fmul_rn(hv.y, g.y));
+        *reinterpret_cast<float2 *>(sm.vals + 2 * c) = z;
+        am = fmaxf(am, fmaxf(fabsf(z.x), fabsf(z.y)));
+        ssc[(c - (int)threadIdx.x) >> 8] = (double)hv.x * hv.x + (double)hv.y * hv.y;
     });
-    float am = 0.0f;
+    static_assert(kR == 256, "chunk slot = (c - thread) / kR");
     double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < kNF; ++i) {
-        const int c = threadIdx.x + i * kR;
-        if (i < nj && c < K / 2) {
-            const float2 hv = *reinterpret_cast<const float2 *>(sm.vals + 2 * c);
-            const float2 g = *reinterpret_cast<const float2 *>(sm.gain + 2 * c);
-            const float2 z = make_float2(__fmul_rn(hv.x, g.x), __fmul_rn(hv.y, g.y));
-            *reinterpret_cast<float2 *>(sm.vals + 2 * c) = z;
-            am = fmaxf(am, fmaxf(fabsf(z.x), fabsf(z.y)));
-            ss += (double)hv.x * hv.x + (double)hv.y * hv.y;
-        }
-    }
+    for (int i = 0; i < kNF; ++i) ss += ssc[i];
     am = wave_max(am);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
