@@ -62,8 +62,8 @@ __global__ __launch_bounds__(kFwThreads) void gemm_few_kernel(
     float *__restrict__ Y, int32_t *__restrict__ acc_out, int ntb, int nrg) {
     constexpr int P = kFwRoundGroups * NR + 1;             // uint4 per staged token row (odd)
     constexpr int kXsU4 = 16 * P;
-    constexpr int kRedU4 = kFwComputeWaves * RB * 4 * 64 / 4;   // int [8][RB][4][64]
-    __shared__ uint4 xs[kXsU4 > kRedU4 ? kXsU4 : kRedU4];
+    __shared__ uint4 xs[kXsU4];
+    __shared__ int red[RB * 4 * 64];                       // the compute waves' sums, [RB][4][64]
     __shared__ float cS[16];                               // fl(gamma * d[token])
     // staging waves past each round, one word per round: a single count
     // could reach 4 (rho + 1) while a slow wave is still in round rho
@@ -77,6 +77,7 @@ __global__ __launch_bounds__(kFwThreads) void gemm_few_kernel(
     const int n0 = 16 * RB * rg;
     if (tid < NR)
         n_staged[tid] = 0u;
+    for (int i = tid; i < RB * 4 * 64; i += kFwThreads) red[i] = 0;
     __syncthreads();                                       // nothing is in flight yet
 
     v4i acc[RB];
@@ -159,24 +160,25 @@ __global__ __launch_bounds__(kFwThreads) void gemm_few_kernel(
         }
     }
 
-    // the eight compute waves' sums (disjoint k) through LDS, then the
-    // 16 RB x mt outputs, a token's columns on consecutive threads
-    __syncthreads();                                       // every wave is done with the codes
-    int *red = reinterpret_cast<int *>(xs);
+    // the eight compute waves' sums (disjoint k) added into LDS with
+    // ds_add (int32 sums are exact, so the order of the adds does not
+    // matter), then the 16 RB x mt outputs, a token's columns on consecutive
+    // threads.  (Each wave's partials written out and summed eight at a time
+    // behind a second barrier: 6.15 / 8.50 against 5.92 / 8.15 us at
+    // K2560 -> N6912, M = 32 / 64.)
     if (wave >= kFwStageThreads / 64) {
-        const int cw = wave - kFwStageThreads / 64;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) red[((cw * RB + rb) * 4 + v) * 64 + lane] = acc[rb][v];
+            for (int v = 0; v < 4; ++v)
+                __hip_atomic_fetch_add(&red[(rb * 4 + v) * 64 + lane], acc[rb][v], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
     for (int o = tid; o < 256 * RB; o += kFwThreads) {
         const int tok = o / (16 * RB), c = o % (16 * RB);
         const int rb = c >> 4, l = 16 * (tok >> 2) + (c & 15), v = tok & 3;
-        int sum = 0;
-#pragma unroll
-        for (int cw = 0; cw < kFwComputeWaves; ++cw) sum += red[((cw * RB + rb) * 4 + v) * 64 + l];
+        const int sum = red[(rb * 4 + v) * 64 + l];
         const int col = n0 + c;
         if (tok < mt && col < N) {
             const size_t off = (size_t)(m0 + tok) * N + col;
