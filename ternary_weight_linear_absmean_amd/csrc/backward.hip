@@ -91,13 +91,24 @@ __global__ __launch_bounds__(256) void transpose_scale_split_kernel(const float 
     __shared__ float s[kTile][kTile + 1];
     const int t = threadIdx.x;
     const int m0 = (int)(blockIdx.x % m_tiles) * kTile, n0 = (int)(blockIdx.x / m_tiles) * kTile;
+    // Every load first, unconditional at clamped (in-bounds) addresses
+    // (M, N >= 1 here), then the products: with a branch around each load
+    // the compiler waited for every load before issuing the next.
+    constexpr int kPer = kTile * kTile / 256;
+    float yv[kPer], dv[kPer];
 #pragma unroll
-    for (int p = 0; p < kTile * kTile / 256; ++p) {
+    for (int p = 0; p < kPer; ++p) {
         const int e = t + 256 * p;
         const int r = e >> 6, c = e & 63;                 // dY row m0 + r, column n0 + c
-        float v = 0.0f;
-        if (m0 + r < M && n0 + c < N) v = __fmul_rn(dY[(size_t)(m0 + r) * N + n0 + c], d[m0 + r]);
-        s[c][r] = v;
+        const int rr = min(m0 + r, M - 1), cc = min(n0 + c, N - 1);
+        yv[p] = dY[(size_t)rr * N + cc];
+        dv[p] = d[rr];
+    }
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+        const int e = t + 256 * p;
+        const int r = e >> 6, c = e & 63;
+        s[c][r] = (m0 + r < M && n0 + c < N) ? __fmul_rn(yv[p], dv[p]) : 0.0f;
     }
     __syncthreads();
 #pragma unroll
