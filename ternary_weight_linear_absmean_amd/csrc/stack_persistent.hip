@@ -251,11 +251,19 @@ __device__ __forceinline__ bool receive(const PArgs &a, const uint2 *p0, unsigne
     for (int i = 0; i < NC; ++i)
         if (i < nj && r + i * kR < nch) pending |= 1u << i;
     const uint64_t start = __builtin_amdgcn_s_memrealtime();
-    // While the producers are still working, only lane 0 of each wave polls
-    // (its first chunk); a sweep by every lane each round would flood the
-    // memory side with re-reads.  The sweep below then reads every chunk.
+    // While the producers are still working, only lane 0 of each wave polls,
+    // on its last chunk (produced by one of the later workgroups: probing
+    // the first chunk, from an early producer, started the sweep while much
+    // of the input was still missing, 585-591 against 568-572 us per token;
+    // every wave probing the input's very last chunk, 585); a sweep by every
+    // lane each round would flood the memory side with re-reads.  The sweep
+    // below then reads every chunk.
     {
-        const int off = idx(2 * r) * 8;
+        int ip = 0;
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+            if (pending >> i & 1u) ip = i;
+        const int off = idx(2 * (r + ip * kR)) * 8;
         for (;;) {
             int rdy = 1;
             if ((threadIdx.x & 63) == 0 && (pending & 1u)) {
